@@ -1,0 +1,147 @@
+"""Pins for the oracle's split partials, their merge, and kv_append (CPU only)."""
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import fp8
+from tests.oracle_cases import oracle_pools
+from workloads import make_case
+
+
+@pytest.mark.parametrize("L,bs", [(1, 16), (15, 16), (16, 16), (17, 16), (100, 16),
+                                  (333, 32), (700, 64), (64, 64)])
+def test_split_bounds_cover_context_once_and_are_page_aligned(L, bs):
+    for S in range(1, 65):
+        b = oracle.split_bounds(L, S, bs)
+        assert len(b) == S
+        covered = []
+        for a, e in b:
+            assert 0 <= a <= e <= L
+            assert a % bs == 0 or a == L
+            covered.extend(range(a, e))
+        assert covered == list(range(L))
+
+
+def test_merge_of_splits_equals_unsplit():
+    w = make_case(3, 8, 2, 32, 16, (1, 77, 300), seed=21)
+    k, v, ks, vs = oracle_pools(w)
+    full = oracle.decode(w.q, k, v, w.block_table, w.context_lens, w.scale)
+    for S in list(range(1, 20)) + [32, 63, 64]:
+        o, lse = oracle.decode_partials(w.q, k, v, w.block_table, w.context_lens,
+                                        w.scale, S)
+        merged = oracle.merge_partials(o, lse)
+        assert np.max(np.abs(merged - full)) < 1e-12, S
+        # sequence of length 1 has one live split only
+        assert np.sum(np.isfinite(lse[0, 0])) == 1
+
+
+def test_one_split_is_identity_and_lse_is_logsumexp():
+    w = make_case(2, 4, 2, 16, 16, (50, 9), seed=22)
+    k, v, _, _ = oracle_pools(w)
+    full = oracle.decode(w.q, k, v, w.block_table, w.context_lens, w.scale)
+    o, lse = oracle.decode_partials(w.q, k, v, w.block_table, w.context_lens,
+                                    w.scale, 1)
+    assert np.max(np.abs(o[:, :, 0] - full)) < 1e-15
+    # lse against scipy's logsumexp over scores gathered by hand
+    for b in range(2):
+        K, _ = w.token_kv(b)
+        for j in range(4):
+            s = w.scale * (K[:, j // 2, :].astype(np.float64) @ w.q[b, j].astype(np.float64))
+            assert abs(lse[b, j, 0] - scipy.special.logsumexp(s)) < 1e-12
+
+
+def test_split_partials_match_scipy_per_chunk():
+    w = make_case(1, 2, 1, 16, 16, (90,), seed=23)
+    k, v, _, _ = oracle_pools(w)
+    S = 4
+    o, lse = oracle.decode_partials(w.q, k, v, w.block_table, w.context_lens,
+                                    w.scale, S)
+    K, V = w.token_kv(0)
+    for i, (a, e) in enumerate(oracle.split_bounds(90, S, 16)):
+        for j in range(2):
+            if e <= a:
+                assert lse[0, j, i] == -np.inf and np.all(o[0, j, i] == 0)
+                continue
+            s = w.scale * (K[a:e, 0].astype(np.float64) @ w.q[0, j].astype(np.float64))
+            p = scipy.special.softmax(s)
+            assert np.max(np.abs(o[0, j, i] - p @ V[a:e, 0].astype(np.float64))) < 1e-14
+            assert abs(lse[0, j, i] - scipy.special.logsumexp(s)) < 1e-12
+
+
+def test_merge_handles_empty_and_all_empty():
+    o = np.zeros((2, 3, 4)); lse = np.full((2, 3), -np.inf)
+    o[0, 1] = [1, 2, 3, 4]; lse[0, 1] = 0.5
+    m = oracle.merge_partials(o, lse)
+    assert np.array_equal(m[0], [1, 2, 3, 4]) and np.array_equal(m[1], [0, 0, 0, 0])
+
+
+def test_context_zero_all_splits_empty():
+    w = make_case(2, 4, 1, 16, 16, (0, 3), seed=24)
+    k, v, _, _ = oracle_pools(w)
+    o, lse = oracle.decode_partials(w.q, k, v, w.block_table, w.context_lens,
+                                    w.scale, 5)
+    assert np.all(lse[0] == -np.inf) and np.all(o[0] == 0)
+    assert np.all(oracle.merge_partials(o, lse)[0] == 0)
+
+
+# -- kv_append ---------------------------------------------------------------
+
+def _append_case(kv_dtype):
+    w = make_case(3, 4, 2, 32, 16, (20, 1, 47), kv_dtype=kv_dtype, seed=25,
+                  extra_pages=2)
+    base_k, base_v, ks, vs = oracle_pools(w, upto_last=True)
+    kn, vn, pos = w.new_tokens()
+    k2, v2 = oracle.kv_append(base_k, base_v, w.block_table, np.arange(3), pos,
+                              kn, vn, kv_dtype, ks, vs)
+    return w, base_k, base_v, k2, v2, kn, vn, pos, ks, vs
+
+
+def _bytes(a):
+    return np.ascontiguousarray(a).view(np.uint8)
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+def test_append_writes_target_slots_only(kv_dtype):
+    w, bk, bv, k2, v2, kn, vn, pos, ks, vs = _append_case(kv_dtype)
+    tk = np.zeros(bk.shape, bool); tv = np.zeros(bv.shape, bool)
+    for b in range(3):
+        p = w.block_table[b, pos[b] // 16]; s = pos[b] % 16
+        tk[p, :, s, :] = True; tv[p, :, :, s] = True
+        for h in range(2):
+            if kv_dtype == "fp16":
+                assert np.array_equal(_bytes(k2[p, h, s]), _bytes(kn[b, h]))
+                assert np.array_equal(_bytes(v2[p, h, :, s]), _bytes(vn[b, h]))
+            else:   # torch's cast as the library reference; it does not
+                    # saturate, so magnitudes >= 448 expect the +-448 code
+                yk = kn[b, h].astype(np.float32) / np.float32(ks[h])
+                yv = vn[b, h].astype(np.float32) / np.float32(vs[h])
+                rk, rv = (np.where(np.abs(y) >= 448, np.where(y < 0, 0xFE, 0x7E),
+                                   torch.from_numpy(np.clip(y, -447, 447)).to(
+                                       torch.float8_e4m3fn).view(torch.uint8).numpy()
+                                   ).astype(np.uint8) for y in (yk, yv))
+                assert np.array_equal(k2[p, h, s], rk)
+                assert np.array_equal(v2[p, h, :, s], rv)
+    # everything else unchanged, byte for byte
+    assert np.array_equal(_bytes(k2[~tk]), _bytes(bk[~tk]))
+    assert np.array_equal(_bytes(v2[~tv]), _bytes(bv[~tv]))
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+def test_append_then_attend_equals_full_pool(kv_dtype):
+    w, bk, bv, k2, v2, kn, vn, pos, ks, vs = _append_case(kv_dtype)
+    fk, fv, _, _ = oracle_pools(w)
+    assert np.array_equal(_bytes(fk), _bytes(k2)) and np.array_equal(_bytes(fv), _bytes(v2))
+
+
+def test_fp8_scales_bound_every_value():
+    w = make_case(2, 4, 2, 32, 16, (40, 12), kv_dtype="fp8_e4m3fn", seed=26)
+    ks, vs = w.fp8_scales()
+    K, V, _, _ = w.tokens()
+    yk = K.astype(np.float32) / ks[None, :, None]
+    # amax / (amax/448) may land one float32 ulp above 448; anything below
+    # 464 rounds to 448 by RNE, so saturation and rounding agree there
+    assert 447.0 <= np.abs(yk).max() < 464.0
+    codes = fp8.quantize(K, ks[None, :, None])
+    assert not np.any(codes == 0x7F) and not np.any(codes == 0xFF)

@@ -1,0 +1,197 @@
+/*
+ * paged_attn.h — C ABI of the MI355X (gfx950) paged MQA/GQA decode library.
+ *
+ * What the library computes (one new token per sequence, decode phase):
+ *
+ *   for every sequence b and query head j, with G = Hq / Hkv and h = j / G,
+ *     out[b, j, :] = softmax_t( scale * q[b, j, :] . K_h[t, :] ) . V_h[t, :]
+ *   over the tokens t = 0 .. context_lens[b]-1 of that sequence, where K_h
+ *   and V_h are gathered page by page through the sequence's block table.
+ *
+ * Sources (page title, section):
+ *   - "TensorRT对Multi-Query Attention的专项优化支持" (r-odyssey.com/news/246352):
+ *     the MHA and MQA formulas (query heads keep their own projection, the
+ *     K/V projection is shared); decode re-reads the whole K/V cache for
+ *     every new token; the cache cut into fixed-length pages.
+ *   - "优化" on tiny-llm (open-infra-ai.github.io/tiny-llm/performance/
+ *     optimization): section 3, kv heads may be fewer than q heads (GQA);
+ *     roadmap table, row 分页 KV (block table, scatter on append, gather on
+ *     read) and row FlashDecoding (long-context decode attention).
+ *   - same tiny-llm page, section 2: the per-sequence KV size
+ *     2 x layers x kv_heads x head_dim x max_seq_len x bytes.
+ * The pages fix no memory layout, head-to-group map, split rule or fp8
+ * format; the choices below are this library's.
+ *
+ * Conventions for every entry point
+ *   - Tensor arguments are DEVICE pointers owned by the caller; `dims` is a
+ *     HOST pointer read during the call only. The library allocates nothing,
+ *     keeps no state between calls and never synchronises: all work is
+ *     enqueued on `stream` (0 = the null stream) in call order.
+ *   - Return value: PA_OK (0) on success, a negative PA_ERR_* code otherwise.
+ *     Arguments are validated on the host BEFORE anything is enqueued; on
+ *     error nothing is enqueued and no output is touched. PA_ERR_HIP means
+ *     the launch itself failed (hipGetLastError after the launch).
+ *   - Device-data contracts (not checked on the host, which never reads
+ *     device memory): for every sequence, block_table entries 0 ..
+ *     ceil(L/bs)-1 are page ids in [0, num_pages), and 0 <= L <=
+ *     max_blocks_per_seq * block_size. Kernels clamp L into that range and
+ *     page ids into [0, num_pages), so a bad table can give wrong numbers
+ *     but never reads or writes outside the caller's buffers.
+ *   - Supported shapes: head_dim 64 or 128; block_size 16, 32 or 64;
+ *     num_q_heads a multiple of num_kv_heads with G = Hq/Hkv <= 128.
+ *
+ * Memory layouts (row-major, densely packed):
+ *   q, out          [B, Hq, d]            fp16
+ *   k_pages         [P, Hkv, bs, d]       token-major inside a page
+ *   v_pages         [P, Hkv, d, bs]       dimension-major inside a page
+ *   block_table     [B, max_blocks_per_seq] int32 page ids
+ *   context_lens    [B]                   int32 tokens per sequence
+ *   k_scale,v_scale [Hkv]                 fp32, fp8 caches only (else NULL)
+ * fp8 caches hold OCP E4M3FN codes (1 byte, max 448, no infinities); the
+ * value of a code is decode(code) * scale[h].
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum pa_kv_dtype {
+  PA_KV_FP16 = 0,        /* IEEE binary16 */
+  PA_KV_FP8_E4M3FN = 1,  /* OCP E4M3FN code + per-kv-head fp32 scale */
+};
+
+enum pa_status {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,       /* a required pointer is NULL */
+  PA_ERR_SHAPE = -2,      /* unsupported or inconsistent sizes */
+  PA_ERR_DTYPE = -3,      /* unknown kv_dtype, or scales missing for fp8 */
+  PA_ERR_SPLITS = -4,     /* num_splits outside [1, PA_MAX_SPLITS] */
+  PA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required */
+  PA_ERR_HIP = -6,        /* the kernel launch failed */
+};
+
+#define PA_MAX_SPLITS 1024
+
+/* Sizes shared by every call on one cache. num_seqs may be 0 (no work). */
+typedef struct pa_dims {
+  int32_t num_seqs;            /* B   */
+  int32_t num_q_heads;         /* Hq  */
+  int32_t num_kv_heads;        /* Hkv */
+  int32_t head_dim;            /* d   */
+  int32_t block_size;          /* bs, tokens per page */
+  int32_t num_pages;           /* P, pages in each of k_pages / v_pages */
+  int32_t max_blocks_per_seq;  /* row length of block_table */
+  int32_t kv_dtype;            /* enum pa_kv_dtype */
+} pa_dims;
+
+/*
+ * kv_append — scatter new tokens' K and V into their pages.
+ *
+ * Source: tiny-llm "优化", roadmap row 分页 KV (scatter through the block
+ * table on write) and section 5 (the append position is a per-step device
+ * value); per-tensor K/V scales: "TensorRT对Multi-Query Attention的专项优化
+ * 支持", quantisation paragraph.
+ *
+ * Token i (0 <= i < num_tokens) belongs to sequence s = seq_ids[i] (or
+ * s = i when seq_ids is NULL, which requires num_tokens <= num_seqs) and
+ * position p = positions[i]; its row k_new[i, h, :] is stored at
+ *   k_pages[block_table[s, p / bs], h, p % bs, :]
+ * and v_new[i, h, :] at v_pages[block_table[s, p / bs], h, :, p % bs].
+ *   k_new, v_new : [num_tokens, Hkv, d] fp16, device
+ *   fp16 cache   : the fp16 bits are copied unchanged
+ *   fp8 cache    : code = RNE_e4m3fn(float(x) / k_scale[h]) (IEEE fp32
+ *                  division; magnitudes >= 448 saturate to +-448, NaN -> 0x7F)
+ * Only the addressed slots are written. Two tokens addressing one slot is
+ * undefined. positions[i] must be < max_blocks_per_seq * bs (out-of-range
+ * positions or sequence ids are skipped).
+ */
+int kv_append(const pa_dims* dims, int32_t num_tokens,
+              const void* k_new, const void* v_new,
+              const int32_t* seq_ids, const int32_t* positions,
+              const int32_t* block_table,
+              const float* k_scale, const float* v_scale,
+              void* k_pages, void* v_pages, hipStream_t stream);
+
+/*
+ * paged_decode_attn — single-pass decode attention.
+ *
+ * Source: MHA/MQA formulas and the decode re-read paragraph of
+ * "TensorRT对Multi-Query Attention的专项优化支持"; GQA (section 3) and the
+ * paged gather (roadmap row 分页 KV) of tiny-llm "优化".
+ *
+ * One workgroup per (sequence, kv head) covers that sequence's whole
+ * context; `out` [B, Hq, d] fp16 receives the normalised result, rounded
+ * to nearest even. Sequences with L = 0 get zeros. `scale` multiplies
+ * q . k (typically 1/sqrt(d)). k_scale / v_scale: fp8 caches only.
+ */
+int paged_decode_attn(const pa_dims* dims, const void* q,
+                      const void* k_pages, const void* v_pages,
+                      const int32_t* block_table, const int32_t* context_lens,
+                      float scale, const float* k_scale, const float* v_scale,
+                      void* out, hipStream_t stream);
+
+/*
+ * Workspace bytes needed by paged_decode_attn_splitk for num_splits splits:
+ *   o   float32 [B, Hq, S, d]   (first)
+ *   lse float32 [B, Hq, S]      (directly after o)
+ * Returns 0 for invalid dims or num_splits.
+ */
+size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
+                                               int32_t num_splits);
+
+/*
+ * paged_decode_attn_splitk — first pass of split-K decode attention.
+ *
+ * Source: tiny-llm "优化", roadmap row FlashDecoding (long-context decode
+ * attention; the page names it only). Split rule (this library's): split i
+ * of a sequence with L tokens covers tokens [i*C, min((i+1)*C, L)) where
+ * C = bs * ceil(ceil(L / S) / bs) (page-aligned equal chunks). For every
+ * (b, j, i) it writes the split's normalised output o[b, j, i, :] and
+ * lse[b, j, i] = ln(sum_t exp(scale * q . k_t)) over the split's tokens;
+ * an empty split writes o = 0 and lse = -inf. Every element of the
+ * workspace's o and lse regions is written.
+ */
+int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
+                             const void* k_pages, const void* v_pages,
+                             const int32_t* block_table,
+                             const int32_t* context_lens, float scale,
+                             const float* k_scale, const float* v_scale,
+                             int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * paged_decode_attn_splitk_reduce — log-sum-exp merge of the splits.
+ *
+ *   out[b, j, :] = sum_i w_i o[b, j, i, :] / sum_i w_i,
+ *   w_i = exp(lse[b, j, i] - max_k lse[b, j, k]);
+ * a row whose splits are all empty gets zeros. Reads the workspace written
+ * by paged_decode_attn_splitk with the same dims and num_splits (enqueue it
+ * after that call on the same stream); writes out [B, Hq, d] fp16.
+ */
+int paged_decode_attn_splitk_reduce(const pa_dims* dims, int32_t num_splits,
+                                    const void* workspace,
+                                    size_t workspace_bytes, void* out,
+                                    hipStream_t stream);
+
+/* Split count the library suggests for a call whose longest context is
+ * max_context_len tokens: enough workgroups to fill the chip's 256 compute
+ * units several times over without splits shorter than a few pages. */
+int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
+                                         int32_t max_context_len);
+
+/* Static description of a status code. Never NULL. */
+const char* pa_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,219 @@
+// C ABI of the paged decode library: host-side validation and dispatch.
+// Declarations, argument meanings, layouts and error behaviour are in
+// include/paged_attn.h. Nothing here allocates, synchronises or reads
+// device memory.
+#include "paged_attn.h"
+
+#include <limits.h>
+
+#include "launch.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+int check_dims(const pa_dims* d) {
+  if (!d) return PA_ERR_NULL;
+  if (d->num_seqs < 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 ||
+      d->num_pages <= 0 || d->max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return PA_ERR_SHAPE;
+  if (d->num_q_heads / d->num_kv_heads > 128) return PA_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return PA_ERR_SHAPE;
+  if (d->block_size != 16 && d->block_size != 32 && d->block_size != 64)
+    return PA_ERR_SHAPE;
+  if ((long long)d->max_blocks_per_seq * d->block_size > INT_MAX)
+    return PA_ERR_SHAPE;
+  if ((long long)d->num_pages * d->num_kv_heads > INT_MAX) return PA_ERR_SHAPE;
+  if (d->kv_dtype != PA_KV_FP16 && d->kv_dtype != PA_KV_FP8_E4M3FN)
+    return PA_ERR_DTYPE;
+  return PA_OK;
+}
+
+int check_scales(const pa_dims* d, const float* ks, const float* vs) {
+  if (d->kv_dtype == PA_KV_FP8_E4M3FN && (!ks || !vs)) return PA_ERR_DTYPE;
+  return PA_OK;
+}
+
+pa::AttnArgs make_args(const pa_dims* d, const void* q, const void* kp,
+                       const void* vp, const int32_t* bt, const int32_t* lens,
+                       float scale, const float* ks, const float* vs) {
+  pa::AttnArgs a{};
+  a.q = static_cast<const _Float16*>(q);
+  a.k_pages = static_cast<const uint8_t*>(kp);
+  a.v_pages = static_cast<const uint8_t*>(vp);
+  a.block_table = bt;
+  a.context_lens = lens;
+  a.k_scale = ks;
+  a.v_scale = vs;
+  a.scale_log2 = scale * kLog2e;
+  a.B = d->num_seqs;
+  a.Hq = d->num_q_heads;
+  a.Hkv = d->num_kv_heads;
+  a.G = d->num_q_heads / d->num_kv_heads;
+  a.P = d->num_pages;
+  a.max_blocks = d->max_blocks_per_seq;
+  return a;
+}
+
+size_t ws_bytes(const pa_dims* d, int32_t S) {
+  const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
+  return rows * (size_t)d->head_dim * sizeof(float) + rows * sizeof(float);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int kv_append(const pa_dims* dims, int32_t num_tokens, const void* k_new,
+              const void* v_new, const int32_t* seq_ids,
+              const int32_t* positions, const int32_t* block_table,
+              const float* k_scale, const float* v_scale, void* k_pages,
+              void* v_pages, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (!seq_ids && num_tokens > dims->num_seqs) return PA_ERR_SHAPE;
+  if ((long long)num_tokens * dims->num_kv_heads * (dims->head_dim / 2) >
+      (long long)INT_MAX * 256)
+    return PA_ERR_SHAPE;
+  if (!k_new || !v_new || !positions || !block_table || !k_pages || !v_pages)
+    return PA_ERR_NULL;
+  rc = check_scales(dims, k_scale, v_scale);
+  if (rc) return rc;
+  if (num_tokens == 0 || dims->num_seqs == 0) return PA_OK;
+  pa::KvAppendArgs a{};
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.seq_ids = seq_ids;
+  a.positions = positions;
+  a.block_table = block_table;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_pages = static_cast<uint8_t*>(k_pages);
+  a.v_pages = static_cast<uint8_t*>(v_pages);
+  a.num_tokens = num_tokens;
+  a.B = dims->num_seqs;
+  a.Hkv = dims->num_kv_heads;
+  a.bs = dims->block_size;
+  a.P = dims->num_pages;
+  a.max_blocks = dims->max_blocks_per_seq;
+  return hip_status(pa::launch_kv_append(a, dims->head_dim,
+                                         dims->kv_dtype == PA_KV_FP8_E4M3FN,
+                                         stream));
+}
+
+int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
+                      const void* v_pages, const int32_t* block_table,
+                      const int32_t* context_lens, float scale,
+                      const float* k_scale, const float* v_scale, void* out,
+                      hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
+    return PA_ERR_NULL;
+  rc = check_scales(dims, k_scale, v_scale);
+  if (rc) return rc;
+  if ((long long)dims->num_seqs * dims->num_kv_heads > INT_MAX) return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0) return PA_OK;
+  pa::AttnArgs a = make_args(dims, q, k_pages, v_pages, block_table,
+                             context_lens, scale, k_scale, v_scale);
+  a.out = static_cast<_Float16*>(out);
+  a.S = 1;
+  a.split = 0;
+  return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
+                                    dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+}
+
+size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
+                                               int32_t num_splits) {
+  if (check_dims(dims) != PA_OK) return 0;
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return 0;
+  return ws_bytes(dims, num_splits);
+}
+
+int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
+                             const void* k_pages, const void* v_pages,
+                             const int32_t* block_table,
+                             const int32_t* context_lens, float scale,
+                             const float* k_scale, const float* v_scale,
+                             int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens)
+    return PA_ERR_NULL;
+  rc = check_scales(dims, k_scale, v_scale);
+  if (rc) return rc;
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
+  if ((long long)dims->num_seqs * dims->num_kv_heads * num_splits > INT_MAX)
+    return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
+    return PA_ERR_WORKSPACE;
+  pa::AttnArgs a = make_args(dims, q, k_pages, v_pages, block_table,
+                             context_lens, scale, k_scale, v_scale);
+  const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads * num_splits;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = a.ws_o + rows * dims->head_dim;
+  a.S = num_splits;
+  a.split = 1;
+  return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
+                                    dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+}
+
+int paged_decode_attn_splitk_reduce(const pa_dims* dims, int32_t num_splits,
+                                    const void* workspace,
+                                    size_t workspace_bytes, void* out,
+                                    hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out) return PA_ERR_NULL;
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
+  if ((long long)dims->num_seqs * dims->num_q_heads > INT_MAX) return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
+    return PA_ERR_WORKSPACE;
+  pa::ReduceArgs a{};
+  const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads * num_splits;
+  a.ws_o = static_cast<const float*>(workspace);
+  a.ws_lse = a.ws_o + rows * dims->head_dim;
+  a.out = static_cast<_Float16*>(out);
+  a.rows = dims->num_seqs * dims->num_q_heads;
+  a.S = num_splits;
+  return hip_status(pa::launch_reduce(a, dims->head_dim, stream));
+}
+
+int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
+                                         int32_t max_context_len) {
+  if (check_dims(dims) != PA_OK || max_context_len <= 0) return 1;
+  // aim for ~2048 workgroups (8 per compute unit on 256 CUs) while keeping
+  // every split at least 8 pages long
+  const long long wgs = (long long)dims->num_seqs * dims->num_kv_heads;
+  long long S = (2048 + wgs - 1) / (wgs > 0 ? wgs : 1);
+  const long long min_chunk = 8LL * dims->block_size;
+  const long long max_S = (max_context_len + min_chunk - 1) / min_chunk;
+  if (S > max_S) S = max_S;
+  if (S < 1) S = 1;
+  if (S > PA_MAX_SPLITS) S = PA_MAX_SPLITS;
+  return (int32_t)S;
+}
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SHAPE: return "unsupported or inconsistent sizes";
+    case PA_ERR_DTYPE: return "unknown kv dtype or fp8 scales missing";
+    case PA_ERR_SPLITS: return "num_splits outside [1, PA_MAX_SPLITS]";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t pa_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Device helpers shared by the gfx950 kernels of the paged decode library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16x16x32 fp16 MFMA, fp32 accumulate. Operand layout on gfx950 (checked on
+// the device): A row = lane % 16, B column = lane % 16, and the 8 values a
+// lane holds are K-slots 8 * (lane / 16) + 0..7 for both A and B; the
+// result holds column lane % 16, rows 4 * (lane / 16) + 0..3.
+__device__ __forceinline__ f32x4 mfma_16x16x32(half8 a, half8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 as_half8(u32x4 v) {
+  return __builtin_bit_cast(half8, v);
+}
+
+// Two e4m3fn codes sitting in the low bytes of the two 16-bit halves of `t`
+// become two fp16 values equal to code_value * 2^-8, exactly: the 4-bit
+// exponent and 3-bit mantissa land in fp16's exponent/mantissa fields, so
+// fp16's bias (15) versus e4m3's (7) scales every value, subnormals
+// included, by 2^-8. Codes 0x7F/0xFF (NaN) come out as finite 1.875.
+__device__ __forceinline__ uint32_t e4m3_pair_to_f16_pair(uint32_t t) {
+  return ((t & 0x007F007Fu) << 7) | ((t & 0x00800080u) << 8);
+}
+
+// Four codes (one dword, byte i = code i) -> four fp16 (two dwords).
+__device__ __forceinline__ u32x2 e4m3x4_to_f16x4(uint32_t w) {
+  uint32_t lo = (w & 0xFFu) | ((w & 0xFF00u) << 8);
+  uint32_t hi = ((w >> 16) & 0xFFu) | ((w >> 8) & 0xFF0000u);
+  u32x2 r;
+  r.x = e4m3_pair_to_f16_pair(lo);
+  r.y = e4m3_pair_to_f16_pair(hi);
+  return r;
+}
+
+// Eight codes (two dwords) -> one half8 operand (values scaled by 2^-8).
+__device__ __forceinline__ half8 e4m3x8_to_half8(u32x2 w) {
+  u32x2 a = e4m3x4_to_f16x4(w.x);
+  u32x2 b = e4m3x4_to_f16x4(w.y);
+  u32x4 r = {a.x, a.y, b.x, b.y};
+  return as_half8(r);
+}
+
+// float32 -> OCP e4m3fn code, round to nearest even, saturating: written
+// from the format definition (bias 7, 3 mantissa bits, max 448, min normal
+// 2^-6, subnormal quantum 2^-9, NaN = S.1111.111).
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7FFFFFFFu;
+  if (a > 0x7F800000u) return 0x7Fu;                  // NaN
+  if (a >= 0x43E00000u) return sign | 0x7Eu;         // |y| >= 448 -> 448
+  int e = (int)(a >> 23) - 127;
+  if (e >= -6) {                                      // normal range
+    uint32_t m = a & 0x7FFFFFu;
+    uint32_t q = m >> 20;
+    uint32_t rem = m & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) q += 1u;
+    uint32_t ee = (uint32_t)(e + 7);
+    if (q == 8u) { q = 0u; ee += 1u; }
+    return sign | (ee << 3) | q;
+  }
+  // |y| < 2^-6: multiples of 2^-9; the scaling by 512 is exact
+  float t = __uint_as_float(a) * 512.0f;
+  uint32_t k = (uint32_t)__builtin_rintf(t);          // 0..8, 8 = 2^-6
+  return sign | k;
+}
+
+// Cross-lane exchange inside a wave (lane ^ mask), via ds_swizzle-free
+// bpermute: the address is in bytes.
+__device__ __forceinline__ float xor_lanes(float v, int mask) {
+  int lane = (int)__lane_id();
+  return __int_as_float(
+      __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
+}
+
+__device__ __forceinline__ float read_lane(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+
+}  // namespace pa

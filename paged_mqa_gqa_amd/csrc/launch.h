@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct KvAppendArgs {
+  const uint8_t* k_new;      // fp16 [T, Hkv, D]
+  const uint8_t* v_new;
+  const int32_t* seq_ids;    // may be null: token i -> sequence i
+  const int32_t* positions;
+  const int32_t* block_table;
+  const float* k_scale;
+  const float* v_scale;
+  uint8_t* k_pages;
+  uint8_t* v_pages;
+  int num_tokens, B, Hkv, bs, P, max_blocks;
+};
+
+struct AttnArgs {
+  const _Float16* q;         // [B, Hq, D]
+  const uint8_t* k_pages;    // [P, Hkv, BS, D] elements
+  const uint8_t* v_pages;    // [P, Hkv, D, BS] elements
+  const int32_t* block_table;
+  const int32_t* context_lens;
+  const float* k_scale;      // fp8 only
+  const float* v_scale;
+  _Float16* out;             // single pass: [B, Hq, D]
+  float* ws_o;               // split pass: [B, Hq, S, D]
+  float* ws_lse;             // split pass: [B, Hq, S]
+  float scale_log2;          // scale * log2(e)
+  int B, Hq, Hkv, G, P, max_blocks, S;
+  int split;                 // 0: write out, 1: write ws_o / ws_lse
+};
+
+struct ReduceArgs {
+  const float* ws_o;
+  const float* ws_lse;
+  _Float16* out;
+  int rows;                  // B * Hq
+  int S;
+};
+
+hipError_t launch_kv_append(const KvAppendArgs& a, int D, bool fp8,
+                            hipStream_t stream);
+// Returns hipErrorInvalidValue for a shape without a kernel instance.
+hipError_t launch_attn(const AttnArgs& a, int D, int BS, bool fp8,
+                       hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int D, hipStream_t stream);
+
+}  // namespace pa

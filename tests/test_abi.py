@@ -1,0 +1,142 @@
+"""C ABI checks that need no GPU: symbols, status strings, host validation.
+
+Every call here fails validation on the host, which happens before anything
+touches a device, so no GPU is needed. Pointers are dummy non-null values
+that the library must never dereference on these paths.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_mqa_gqa_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pa.library_path()),
+                                reason="library not built")
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
+              "paged_decode_attn_splitk_reduce",
+              "paged_decode_attn_splitk_workspace_size",
+              "paged_decode_attn_suggest_splits", "pa_status_string", "pa_version"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+
+
+def good_dims(**kw):
+    d = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128,
+             block_size=16, num_pages=10, max_blocks_per_seq=4,
+             kv_dtype=pa.KV_FP16)
+    d.update(kw)
+    return pa.PaDims(**d)
+
+
+def attn(d, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, ks=None, vs=None, out=FAKE)
+    args.update(kw)
+    return pa.load().paged_decode_attn(ctypes.byref(d) if d is not None else None,
+                                       args["q"], args["k"], args["v"], args["bt"],
+                                       args["lens"], 0.1, args["ks"], args["vs"],
+                                       args["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=6, num_kv_heads=4), -2),     # Hq % Hkv != 0
+    (dict(head_dim=96), -2),
+    (dict(block_size=8), -2),
+    (dict(block_size=128), -2),
+    (dict(num_kv_heads=0), -2),
+    (dict(num_pages=0), -2),
+    (dict(max_blocks_per_seq=0), -2),
+    (dict(num_seqs=-1), -2),
+    (dict(num_q_heads=2 * 129, num_kv_heads=2), -2),  # G > 128
+    (dict(kv_dtype=7), -3),
+])
+def test_bad_dims_rejected(kw, status):
+    assert attn(good_dims(**kw)) == status
+
+
+def test_null_pointers_rejected():
+    assert attn(None) == -1
+    for key in ["q", "k", "v", "bt", "lens", "out"]:
+        assert attn(good_dims(), **{key: None}) == -1, key
+
+
+def test_fp8_requires_scales():
+    assert attn(good_dims(kv_dtype=pa.KV_FP8_E4M3FN)) == -3
+    assert attn(good_dims(kv_dtype=pa.KV_FP8_E4M3FN), ks=FAKE) == -3
+
+
+def test_empty_batch_is_a_no_op():
+    assert attn(good_dims(num_seqs=0)) == 0
+
+
+def test_splitk_validation():
+    lib = pa.load()
+    d = good_dims()
+    need = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 4)
+    assert need == 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4
+    assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 0) == 0
+    call = lambda S, ws, n: lib.paged_decode_attn_splitk(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, S, ws, n, None)
+    assert call(0, FAKE, need) == -4
+    assert call(1025, FAKE, 10 ** 9) == -4
+    assert call(4, FAKE, need - 1) == -5
+    assert call(4, None, need) == -5
+    red = lambda S, ws, n, out=FAKE: lib.paged_decode_attn_splitk_reduce(
+        ctypes.byref(d), S, ws, n, out, None)
+    assert red(4, FAKE, need - 4) == -5
+    assert red(0, FAKE, need) == -4
+    assert red(4, FAKE, need, None) == -1
+
+
+def test_kv_append_validation():
+    lib = pa.load()
+    d = good_dims()
+    call = lambda T, sid=FAKE, **kw: lib.kv_append(
+        ctypes.byref(d), T, kw.get("k", FAKE), FAKE, sid, FAKE, FAKE,
+        kw.get("ks"), kw.get("vs"), FAKE, FAKE, None)
+    assert call(-1) == -2
+    assert call(3, sid=None) == -2          # T > B without seq_ids
+    assert call(2, k=None) == -1
+    assert call(0) == 0                     # nothing to do
+    d8 = good_dims(kv_dtype=pa.KV_FP8_E4M3FN)
+    assert lib.kv_append(ctypes.byref(d8), 1, FAKE, FAKE, None, FAKE, FAKE, None,
+                         None, FAKE, FAKE, None) == -3
+
+
+def test_status_strings_and_version():
+    for s in [0, -1, -2, -3, -4, -5, -6, -99]:
+        assert isinstance(pa.status_string(s), str) and pa.status_string(s)
+    assert pa.version() >= 100
+
+
+def test_suggest_splits():
+    d = pa.PaDims(32, 32, 8, 128, 16, 5000, 256, pa.KV_FP16)
+    s = pa.suggest_splits(d, 4096)
+    assert 1 <= s <= 32
+    d4 = pa.PaDims(4, 32, 8, 128, 64, 9000, 2048, pa.KV_FP16)
+    assert pa.suggest_splits(d4, 131072) >= 16
+    assert pa.suggest_splits(d4, 1) == 1

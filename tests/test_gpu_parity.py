@@ -1,0 +1,289 @@
+"""GPU parity: the HIP library against the fp64 CPU oracle (needs an MI355X).
+
+Both sides get the same seeded inputs from `workloads`; the oracle builds
+its pools with its own append, the GPU with the library's kv_append, and no
+expected value comes from the GPU. Tolerances are those fixed for the path:
+max-abs 2e-3 for fp16 KV and 3e-2 for fp8 KV (fp32 accumulation), cache
+append and block-table indexing bit-exact.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import fp8 as ofp8
+from tests.oracle_cases import oracle_pools
+from workloads import CONFIGS, make, make_case
+from workloads.device import DeviceWorkload, remap_pages
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": 2e-3, "fp8_e4m3fn": 3e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_mqa_gqa_amd as pa
+    pa.load()          # must load on a GPU machine: no fallback exists
+    yield
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+def pa_mod():
+    import paged_mqa_gqa_amd as pa
+    return pa
+
+
+def gpu_decode(dw, num_splits=1):
+    pa = pa_mod()
+    if num_splits == 1:
+        out = pa.paged_decode_attn(dw.q, dw.k_pages, dw.v_pages, dw.block_table,
+                                   dw.context_lens, dw.scale, dw.k_scale, dw.v_scale)
+    else:
+        ws = pa.paged_decode_attn_splitk(dw.q, dw.k_pages, dw.v_pages, dw.block_table,
+                                         dw.context_lens, dw.scale, num_splits,
+                                         dw.k_scale, dw.v_scale)
+        out = pa.paged_decode_attn_splitk_reduce(dw.q, dw.k_pages, dw.block_table,
+                                                 num_splits, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_out(w, seqs=None):
+    if seqs is None:
+        k, v, ks, vs = oracle_pools(w)
+        return oracle.decode(w.q, k, v, w.block_table, w.context_lens, w.scale,
+                             w.cfg.kv_dtype, ks, vs)
+    sub = remap_pages(w, seqs)
+    k, v, ks, vs = oracle_pools(sub, seqs=seqs)
+    return oracle.decode(sub.q, k, v, sub.block_table, sub.context_lens, sub.scale,
+                         sub.cfg.kv_dtype, ks, vs, seqs=seqs)
+
+
+def max_err(gpu_out, ref, seqs=None):
+    g = gpu_out.float().cpu().numpy().astype(np.float64)
+    if seqs is not None:
+        g, ref = g[list(seqs)], ref[list(seqs)]
+    assert np.all(np.isfinite(g)), "non-finite output"
+    return float(np.max(np.abs(g - ref))) if g.size else 0.0
+
+
+# -- cache append ----------------------------------------------------------
+
+APPEND_CASES = [
+    dict(num_seqs=3, num_q_heads=4, num_kv_heads=2, head_dim=128, block_size=16, lens=(20, 1, 47)),
+    dict(num_seqs=2, num_q_heads=8, num_kv_heads=4, head_dim=64, block_size=32, lens=(33, 90)),
+    dict(num_seqs=4, num_q_heads=8, num_kv_heads=8, head_dim=128, block_size=64, lens=(64, 65, 1, 200)),
+]
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("case", range(len(APPEND_CASES)))
+def test_kv_append_bit_exact(case, kv_dtype):
+    c = APPEND_CASES[case]
+    say("kv_append", kv_dtype, c)
+    w = make_case(**c, kv_dtype=kv_dtype, seed=31 + case, extra_pages=3)
+    dw = DeviceWorkload(w, upto_last=True)       # library fills all but the last token
+    pa = pa_mod()
+    pa.kv_append(dw.new_k, dw.new_v, dw.k_pages, dw.v_pages, dw.block_table,
+                 dw.positions, k_scale=dw.k_scale, v_scale=dw.v_scale)
+    torch.cuda.synchronize()
+    ok, ov, _, _ = oracle_pools(w)
+    gk = dw.k_pages.cpu().numpy().view(np.uint8)
+    gv = dw.v_pages.cpu().numpy().view(np.uint8)
+    assert np.array_equal(gk, np.ascontiguousarray(ok).view(np.uint8))
+    assert np.array_equal(gv, np.ascontiguousarray(ov).view(np.uint8))
+
+
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** -8, 0.010296, 3.7])
+def test_kv_append_fp8_encodes_every_fp16_pattern(scale):
+    """All 65536 fp16 bit patterns (incl. inf/NaN) through the device encoder."""
+    say("fp8 encode exhaustive", scale)
+    pa = pa_mod()
+    vals = np.arange(65536, dtype=np.uint16).view(np.float16)
+    T, H, D, bs = 512, 1, 128, 16
+    x = vals.reshape(T, H, D)
+    bt = np.arange(T // bs, dtype=np.int32)[None, :]
+    P = T // bs
+    kp = torch.zeros((P, H, bs, D), dtype=torch.uint8, device="cuda")
+    vp = torch.zeros((P, H, D, bs), dtype=torch.uint8, device="cuda")
+    s = torch.tensor([scale], dtype=torch.float32, device="cuda")
+    xt = torch.from_numpy(x.copy()).cuda()
+    pa.kv_append(xt, xt, kp, vp, torch.from_numpy(bt).cuda(),
+                 torch.arange(T, dtype=torch.int32, device="cuda"),
+                 seq_ids=torch.zeros(T, dtype=torch.int32, device="cuda"),
+                 k_scale=s, v_scale=s)
+    torch.cuda.synchronize()
+    ref = ofp8.quantize(x, np.float32(scale))           # [T, 1, D]
+    gk = kp.cpu().numpy()                               # [P, 1, bs, D]
+    got_k = gk.reshape(T, H, D)
+    assert np.array_equal(got_k, ref)
+    got_v = vp.cpu().numpy().transpose(0, 3, 1, 2).reshape(T, H, D)
+    assert np.array_equal(got_v, ref)
+
+
+def test_fp8_decode_of_every_code_via_single_token_attention():
+    """L = 1 returns V exactly: out = fp16(decode(code) * v_scale) for every code."""
+    say("fp8 decode exhaustive")
+    pa = pa_mod()
+    H, D, bs = 2, 128, 16
+    codes = np.arange(256, dtype=np.uint8).reshape(H, D)
+    vp = np.zeros((1, H, D, bs), np.uint8)
+    vp[0, :, :, 0] = codes
+    kp = np.zeros((1, H, bs, D), np.uint8)
+    vscale = np.array([0.75, 0.0103], np.float32)
+    out = pa.paged_decode_attn(
+        torch.zeros((1, H, D), dtype=torch.float16, device="cuda"),
+        torch.from_numpy(kp).cuda(), torch.from_numpy(vp).cuda(),
+        torch.zeros((1, 1), dtype=torch.int32, device="cuda"),
+        torch.ones(1, dtype=torch.int32, device="cuda"), 0.1,
+        torch.ones(H, dtype=torch.float32, device="cuda"),
+        torch.from_numpy(vscale).cuda())
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()[0].astype(np.float64)
+    exp = (ofp8.decode(codes) * vscale[:, None].astype(np.float64)).astype(np.float16).astype(np.float64)
+    fin = np.isfinite(exp)                      # 0x7F / 0xFF are NaN codes, never stored
+    assert fin.sum() == 254
+    # the device scales in fp32 and then rounds to fp16: at most 1 fp16 ulp apart
+    ulp = np.spacing(np.abs(exp[fin]).astype(np.float16)).astype(np.float64)
+    assert np.all(np.abs(got[fin] - exp[fin]) <= ulp)
+
+
+# -- attention parity ------------------------------------------------------
+
+SWEEP = [
+    # (Hq, Hkv, d, bs, lens)
+    (4, 1, 64, 16, (17, 40)),
+    (4, 4, 128, 16, (1, 2, 15, 16, 17, 31, 32, 33)),
+    (8, 2, 128, 32, (100, 300, 64, 65)),
+    (32, 8, 128, 16, (700, 1, 513)),
+    (16, 1, 128, 64, (1000, 63, 64, 129)),
+    (20, 1, 64, 16, (90, 33)),
+    (48, 2, 128, 32, (257, 12)),
+    (96, 1, 128, 32, (600, 31, 1)),
+    (128, 1, 64, 16, (77, 300)),
+    (2, 1, 64, 64, (5000,)),
+    (8, 8, 64, 16, (0, 5, 0)),
+]
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_decode_parity_sweep(case, kv_dtype):
+    Hq, Hkv, d, bs, lens = SWEEP[case]
+    say("decode", kv_dtype, SWEEP[case])
+    w = make_case(len(lens), Hq, Hkv, d, bs, lens, kv_dtype=kv_dtype,
+                  seed=100 + case, extra_pages=2)
+    dw = DeviceWorkload(w)
+    ref = oracle_out(w)
+    err = max_err(gpu_decode(dw), ref)
+    assert err <= TOL[kv_dtype], err
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 16, 64])
+def test_splitk_partials_and_merge(S, kv_dtype):
+    say("splitk", kv_dtype, S)
+    pa = pa_mod()
+    lens = (1, 40, 333, 1000, 0)
+    w = make_case(len(lens), 8, 2, 128, 16, lens, kv_dtype=kv_dtype, seed=200 + S)
+    dw = DeviceWorkload(w)
+    ws = pa.paged_decode_attn_splitk(dw.q, dw.k_pages, dw.v_pages, dw.block_table,
+                                     dw.context_lens, dw.scale, S, dw.k_scale, dw.v_scale)
+    out = pa.paged_decode_attn_splitk_reduce(dw.q, dw.k_pages, dw.block_table, S, ws)
+    torch.cuda.synchronize()
+    o_g, lse_g = pa.split_views(ws, len(lens), 8, S, 128)
+    o_g = o_g.cpu().numpy().astype(np.float64)
+    lse_g = lse_g.cpu().numpy().astype(np.float64)
+    k, v, ks, vs = oracle_pools(w)
+    o_r, lse_r = oracle.decode_partials(w.q, k, v, w.block_table, w.context_lens,
+                                        w.scale, S, kv_dtype, ks, vs)
+    assert np.array_equal(np.isinf(lse_g), np.isinf(lse_r))     # same empty splits
+    live = np.isfinite(lse_r)
+    assert np.max(np.abs(lse_g[live] - lse_r[live])) <= 1e-3
+    assert np.max(np.abs(o_g - o_r)) <= TOL[kv_dtype]
+    full = oracle.decode(w.q, k, v, w.block_table, w.context_lens, w.scale,
+                         kv_dtype, ks, vs)
+    assert max_err(out, full) <= TOL[kv_dtype]
+
+
+def test_output_bitwise_invariant_under_page_permutation():
+    say("page permutation")
+    lens = (300, 77, 1000)
+    outs = []
+    for seed_pages in range(3):
+        w = make_case(3, 16, 2, 128, 16, lens, seed=300)
+        # re-draw only the page map: permute physical pages of the same tokens
+        rng = np.random.default_rng(seed_pages)
+        perm = rng.permutation(w.num_pages)
+        w.block_table = perm[w.block_table].astype(np.int32)
+        dw = DeviceWorkload(w)
+        outs.append(gpu_decode(dw).cpu())
+        outs.append(gpu_decode(dw, 5).cpu())
+    for o in outs[2::2]:
+        assert torch.equal(o, outs[0])
+    for o in outs[3::2]:
+        assert torch.equal(o, outs[1])
+
+
+def test_repeated_calls_are_deterministic():
+    say("determinism")
+    w = make_case(4, 32, 8, 128, 16, (2000, 1, 640, 333), seed=301)
+    dw = DeviceWorkload(w)
+    a = [gpu_decode(dw).cpu() for _ in range(3)] + [gpu_decode(dw, 4).cpu() for _ in range(3)]
+    assert all(torch.equal(a[0], x) for x in a[1:3])
+    assert all(torch.equal(a[3], x) for x in a[4:6])
+
+
+def test_decode_step_append_then_attend():
+    """One decode step as the hot path runs it: append the new token, attend."""
+    say("append+attend step")
+    for kv_dtype in ["fp16", "fp8_e4m3fn"]:
+        w = make_case(5, 16, 2, 128, 16, (1, 16, 17, 500, 64), kv_dtype=kv_dtype, seed=302)
+        dw = DeviceWorkload(w, upto_last=True)
+        pa = pa_mod()
+        pa.kv_append(dw.new_k, dw.new_v, dw.k_pages, dw.v_pages, dw.block_table,
+                     dw.positions, k_scale=dw.k_scale, v_scale=dw.v_scale)
+        assert max_err(gpu_decode(dw, 3), oracle_out(w)) <= TOL[kv_dtype]
+
+
+# -- full-size workloads, sampled ------------------------------------------
+
+FULL = {"tiny_mqa": None, "gqa_llama": (0, 7, 31), "wide_mqa": (0, 63),
+        "long_splitk": (2,), "mixed_fp8": None}
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_workload(name):
+    """Each workload at its full size, in the split configuration the benchmark
+    times, after one decode-step append; sampled sequences checked against the
+    oracle (all sequences for the small/fp8 mixes where that stays cheap)."""
+    say("full", name)
+    pa = pa_mod()
+    w = make(name)
+    cfg = w.cfg
+    dw = DeviceWorkload(w, upto_last=True)
+    pa.kv_append(dw.new_k, dw.new_v, dw.k_pages, dw.v_pages, dw.block_table,
+                 dw.positions, k_scale=dw.k_scale, v_scale=dw.v_scale)
+    out = gpu_decode(dw, cfg.num_splits)
+    seqs = FULL[name]
+    if seqs is None and name == "mixed_fp8":
+        rng = np.random.default_rng(0)
+        longest = int(np.argmax(w.context_lens))
+        shortest = int(np.argmin(w.context_lens))
+        seqs = tuple(sorted(set([longest, shortest] + rng.choice(cfg.num_seqs, 6, replace=False).tolist())))
+    ref = oracle_out(w, seqs)
+    err = max_err(out, ref, seqs)
+    say("full", name, "max err", err)
+    assert err <= TOL[cfg.kv_dtype], err
+    # every other row must at least be finite
+    assert torch.isfinite(out.float()).all()

@@ -190,7 +190,7 @@ class Workload:
         ks, vs, sid, pos = [], [], [], []
         for b in seqs:
             k, v = self.token_kv(b)
-            n = k.shape[0] - 1 if upto_last else k.shape[0]
+            n = max(0, k.shape[0] - 1) if upto_last else k.shape[0]
             ks.append(k[:n]); vs.append(v[:n])
             sid.append(np.full(n, b, dtype=np.int32))
             pos.append(np.arange(n, dtype=np.int32))
@@ -200,14 +200,16 @@ class Workload:
     def new_tokens(self):
         """The token each sequence appends in a decode step: its last one.
 
-        Returns K, V fp16 [B, Hkv, d] and positions int32 [B] (= L_b - 1).
+        Returns K, V fp16 [B, Hkv, d] and positions int32 [B] (= L_b - 1;
+        a sequence with L_b = 0 gets position -1, which an append skips).
         """
         cfg = self.cfg
-        k = np.empty((cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim), np.float16)
-        v = np.empty_like(k)
+        k = np.zeros((cfg.num_seqs, cfg.num_kv_heads, cfg.head_dim), np.float16)
+        v = np.zeros_like(k)
         for b in range(cfg.num_seqs):
             kb, vb = self.token_kv(b)
-            k[b] = kb[-1]; v[b] = vb[-1]
+            if kb.shape[0]:
+                k[b] = kb[-1]; v[b] = vb[-1]
         return k, v, (self.context_lens - 1).astype(np.int32)
 
     # -- fp8 calibration --------------------------------------------------
@@ -223,10 +225,13 @@ class Workload:
             if cfg.kv_dtype == "fp8_e4m3fn":
                 for b in range(cfg.num_seqs):
                     k, v = self.token_kv(b)
+                    if k.shape[0] == 0:
+                        continue
                     ka = np.maximum(ka, np.abs(k).max(axis=(0, 2)).astype(np.float32))
                     va = np.maximum(va, np.abs(v).max(axis=(0, 2)).astype(np.float32))
-                ks = ka / np.float32(FP8_E4M3FN_MAX)
-                vs = va / np.float32(FP8_E4M3FN_MAX)
+                # a head with no data at all keeps scale 1
+                ks = np.where(ka > 0, ka / np.float32(FP8_E4M3FN_MAX), np.float32(1))
+                vs = np.where(va > 0, va / np.float32(FP8_E4M3FN_MAX), np.float32(1))
             else:
                 ks = np.ones(H, np.float32); vs = np.ones(H, np.float32)
             self._scales = (ks.astype(np.float32), vs.astype(np.float32))

@@ -40,15 +40,28 @@
  *   - Supported shapes: head_dim 64 or 128; block_size 16, 32 or 64;
  *     num_q_heads a multiple of num_kv_heads with G = Hq/Hkv <= 128.
  *
- * Memory layouts (row-major, densely packed):
- *   q, out          [B, Hq, d]            fp16
- *   k_pages         [P, Hkv, bs, d]       token-major inside a page
- *   v_pages         [P, Hkv, d, bs]       dimension-major inside a page
+ * Memory layouts (densely packed):
+ *   q, out          [B, Hq, d]            fp16, row-major
+ *   k_pages,v_pages [P, Hkv, bs * d]      one tile of bs * d elements per
+ *                                         (page, kv head), in the order below
  *   block_table     [B, max_blocks_per_seq] int32 page ids
  *   context_lens    [B]                   int32 tokens per sequence
  *   k_scale,v_scale [Hkv]                 fp32, fp8 caches only (else NULL)
+ * Inside a tile, slot t (0 <= t < bs) and dimension i (0 <= i < d) sit at
+ * element offset, with blk = t / 16, r = t % 16 and X = 16 bytes / element
+ * size (8 for fp16, 16 for fp8):
+ *   K:  ((blk * (d / X) + i / X) * 16 + r) * X + i % X
+ *   V:  (((blk * (d / 16) + i / 16) * 4 + r / 4) * 16 + i % 16) * 4 + r % 4
+ * i.e. each 16-token block stores K as 16-byte chunks of one token's row,
+ * chunk-major, and V as runs of 4 tokens of one dimension; this is the
+ * order in which the kernels' matrix-core operands are loaded, so every
+ * wave-wide load is one contiguous run. A page pool may be allocated as
+ * [P, Hkv, bs, d] (the binding does), but its last two axes are storage, not
+ * a [token, dim] matrix. Caches are written through kv_append.
  * fp8 caches hold OCP E4M3FN codes (1 byte, max 448, no infinities); the
- * value of a code is decode(code) * scale[h].
+ * value of a code is decode(code) * scale[h]. Device buffers must be
+ * 16-byte aligned (q, k_pages, v_pages, out, workspace) or 4-byte aligned
+ * (k_new, v_new, index arrays, scales).
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -100,9 +113,9 @@ typedef struct pa_dims {
  *
  * Token i (0 <= i < num_tokens) belongs to sequence s = seq_ids[i] (or
  * s = i when seq_ids is NULL, which requires num_tokens <= num_seqs) and
- * position p = positions[i]; its row k_new[i, h, :] is stored at
- *   k_pages[block_table[s, p / bs], h, p % bs, :]
- * and v_new[i, h, :] at v_pages[block_table[s, p / bs], h, :, p % bs].
+ * position p = positions[i]; its row k_new[i, h, :] is stored in the tile
+ * (block_table[s, p / bs], h) of k_pages at slot p % bs (positions per the
+ * layout above), v_new[i, h, :] likewise in v_pages.
  *   k_new, v_new : [num_tokens, Hkv, d] fp16, device
  *   fp16 cache   : the fp16 bits are copied unchanged
  *   fp8 cache    : code = RNE_e4m3fn(float(x) / k_scale[h]) (IEEE fp32
@@ -137,25 +150,35 @@ int paged_decode_attn(const pa_dims* dims, const void* q,
                       void* out, hipStream_t stream);
 
 /*
- * Workspace bytes needed by paged_decode_attn_splitk for num_splits splits:
- *   o   float32 [B, Hq, S, d]   (first)
- *   lse float32 [B, Hq, S]      (directly after o)
+ * Workspace bytes needed by paged_decode_attn_splitk for num_splits partial
+ * slots per (sequence, q head). Layout, densely packed in this order:
+ *   o     float32 [B, Hq, S, d]   normalised partial outputs
+ *   lse   float32 [B, Hq, S]      natural-log sum of exp(scores) per partial
+ *   count int32   [B, Hkv]        partials written for (sequence, kv head)
  * Returns 0 for invalid dims or num_splits.
  */
 size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
                                                int32_t num_splits);
 
 /*
- * paged_decode_attn_splitk — first pass of split-K decode attention.
+ * paged_decode_attn_splitk — first pass of split decode attention.
  *
  * Source: tiny-llm "优化", roadmap row FlashDecoding (long-context decode
- * attention; the page names it only). Split rule (this library's): split i
- * of a sequence with L tokens covers tokens [i*C, min((i+1)*C, L)) where
- * C = bs * ceil(ceil(L / S) / bs) (page-aligned equal chunks). For every
- * (b, j, i) it writes the split's normalised output o[b, j, i, :] and
- * lse[b, j, i] = ln(sum_t exp(scale * q . k_t)) over the split's tokens;
- * an empty split writes o = 0 and lse = -inf. Every element of the
- * workspace's o and lse regions is written.
+ * attention split over the context; the page names it only). The split
+ * is this library's: the 32-token tiles of every (sequence, kv head)
+ * context, laid end to end (sequence-major, then kv head, then position),
+ * are cut into equal contiguous shares, one per workgroup of a persistent
+ * grid, so a ragged batch spreads evenly over the chip. Each (sequence,
+ * kv head) thereby falls into 1..S contiguous token ranges (the share is
+ * widened when needed so that S is never exceeded); for its i-th range
+ * the call writes o[b, j, i, :] (that range's softmax-weighted mean of V)
+ * and lse[b, j, i] = ln(sum over the range of exp(scale * q . k_t)) for
+ * every q head j of the group, and count[b, h] = number of ranges.
+ * Sequences with L = 0 get no ranges (count is then not written).
+ * num_splits == 1 gives one range per (sequence, kv head): the whole
+ * context. num_splits >= 2 should be large enough for the longest context
+ * to span several shares (see paged_decode_attn_suggest_splits); a smaller
+ * value stays correct but leaves part of the grid idle.
  */
 int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
                              const void* k_pages, const void* v_pages,
@@ -166,22 +189,24 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
- * paged_decode_attn_splitk_reduce — log-sum-exp merge of the splits.
+ * paged_decode_attn_splitk_reduce — log-sum-exp merge of the ranges.
  *
  *   out[b, j, :] = sum_i w_i o[b, j, i, :] / sum_i w_i,
- *   w_i = exp(lse[b, j, i] - max_k lse[b, j, k]);
- * a row whose splits are all empty gets zeros. Reads the workspace written
- * by paged_decode_attn_splitk with the same dims and num_splits (enqueue it
- * after that call on the same stream); writes out [B, Hq, d] fp16.
+ *   w_i = exp(lse[b, j, i] - max_k lse[b, j, k]),  i < count[b, j / G];
+ * sequences with context_lens[b] = 0 get zeros. Reads the workspace that
+ * paged_decode_attn_splitk wrote with the same dims, context_lens and
+ * num_splits (enqueue it after that call on the same stream); writes
+ * out [B, Hq, d] fp16, rounded to nearest even.
  */
-int paged_decode_attn_splitk_reduce(const pa_dims* dims, int32_t num_splits,
-                                    const void* workspace,
+int paged_decode_attn_splitk_reduce(const pa_dims* dims,
+                                    const int32_t* context_lens,
+                                    int32_t num_splits, const void* workspace,
                                     size_t workspace_bytes, void* out,
                                     hipStream_t stream);
 
-/* Split count the library suggests for a call whose longest context is
- * max_context_len tokens: enough workgroups to fill the chip's 256 compute
- * units several times over without splits shorter than a few pages. */
+/* num_splits the library suggests for a batch whose longest context is
+ * max_context_len tokens, assuming the batch's mean context is at least
+ * 1/16 of the longest (1 when a single tile covers every context). */
 int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
                                          int32_t max_context_len);
 

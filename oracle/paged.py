@@ -4,12 +4,17 @@ Source: "优化" on tiny-llm, roadmap table, row 分页 KV — K/V are kept in
 fixed-size pages found through a per-sequence block table, written by a
 scatter and read by a gather; "TensorRT对Multi-Query Attention的专项优化支持",
 KV-cache paragraph — long sequences are cut into fixed-length pages. The
-pages give no layout; the library's header fixes it and this file follows it:
+pages give no layout; the library's header fixes it and this file follows it.
 
-  k_pages  [P, Hkv, bs, d]   token-major inside a (page, head) tile
-  v_pages  [P, Hkv, d, bs]   dimension-major inside a (page, head) tile
-  token t of sequence b lives in page block_table[b, t // bs], slot t % bs.
+Pools are arrays [P, Hkv, bs, d] (the allocation shape); the bs * d
+elements of one (page, head) tile are stored in the order below, in units
+of 16-token blocks (blk = t // 16, r = t % 16; X = elements per 16 bytes:
+8 for fp16, 16 for fp8):
 
+  K element (t, i):  ((blk * (d / X) + i // X) * 16 + r) * X + i % X
+  V element (t, i):  (((blk * (d / 16) + i // 16) * 4 + r // 4) * 16 + i % 16) * 4 + r % 4
+
+Token t of sequence b lives in page block_table[b, t // bs], slot t % bs.
 Element type is float16 or the uint8 code of fp8 e4m3fn; for fp8 each kv head
 h has its own float32 scale for K and for V (value = decode(code) * scale).
 """
@@ -20,21 +25,32 @@ import numpy as np
 from . import fp8
 
 
+def chunk_elems(kv_dtype) -> int:
+    return 8 if kv_dtype == "fp16" else 16
+
+
+def k_offset(t, i, d, X):
+    """Element offset of K (slot t, dim i) inside a (page, head) tile."""
+    t = np.asarray(t); i = np.asarray(i)
+    return ((t // 16 * (d // X) + i // X) * 16 + t % 16) * X + i % X
+
+
+def v_offset(t, i, d):
+    """Element offset of V (slot t, dim i) inside a (page, head) tile."""
+    t = np.asarray(t); i = np.asarray(i)
+    r = t % 16
+    return (((t // 16 * (d // 16) + i // 16) * 4 + r // 4) * 16 + i % 16) * 4 + r % 4
+
+
 def empty_pools(num_pages, num_kv_heads, block_size, head_dim, kv_dtype):
     """Pools filled with NaN (fp16 0x7E00, fp8 code 0x7F): never-written slots."""
+    shape = (num_pages, num_kv_heads, block_size, head_dim)
     if kv_dtype == "fp16":
-        k = np.full((num_pages, num_kv_heads, block_size, head_dim), np.nan,
-                    np.float16)
-        v = np.full((num_pages, num_kv_heads, head_dim, block_size), np.nan,
-                    np.float16)
-    elif kv_dtype == "fp8_e4m3fn":
-        k = np.full((num_pages, num_kv_heads, block_size, head_dim),
-                    fp8.NAN_CODE, np.uint8)
-        v = np.full((num_pages, num_kv_heads, head_dim, block_size),
-                    fp8.NAN_CODE, np.uint8)
-    else:
-        raise ValueError(kv_dtype)
-    return k, v
+        return np.full(shape, np.nan, np.float16), np.full(shape, np.nan, np.float16)
+    if kv_dtype == "fp8_e4m3fn":
+        return (np.full(shape, fp8.NAN_CODE, np.uint8),
+                np.full(shape, fp8.NAN_CODE, np.uint8))
+    raise ValueError(kv_dtype)
 
 
 def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
@@ -45,9 +61,10 @@ def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
     fp16 pools receive the bits unchanged; fp8 pools receive
     fp8.quantize(x, scale[h]) per head. Returns new pools (inputs untouched).
     """
-    k_pages = k_pages.copy()
-    v_pages = v_pages.copy()
-    bs = k_pages.shape[2]
+    P, H, bs, d = k_pages.shape
+    X = chunk_elems(kv_dtype)
+    kf = k_pages.copy().reshape(P, H, bs * d)
+    vf = v_pages.copy().reshape(P, H, bs * d)
     seq_ids = np.asarray(seq_ids, np.int64)
     positions = np.asarray(positions, np.int64)
     page = np.asarray(block_table, np.int64)[seq_ids, positions // bs]
@@ -60,22 +77,28 @@ def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
         vs = np.asarray(v_scale, np.float32)[None, :, None]
         kw = fp8.quantize(k_new, ks)
         vw = fp8.quantize(v_new, vs)
-    # k_pages[page, :, slot, :] has shape [T, Hkv, d]; so does the V view
-    # v_pages[page, :, :, slot] ([T, Hkv, d] after advanced indexing).
-    k_pages[page, :, slot, :] = kw
-    v_pages[page, :, :, slot] = vw
-    return k_pages, v_pages
+    dims = np.arange(d)
+    ko = k_offset(slot[:, None], dims[None, :], d, X)         # [T, d]
+    vo = v_offset(slot[:, None], dims[None, :], d)
+    # kf[page, :, ko] -> [T, d, Hkv] (advanced indices first), so transpose
+    kf[page[:, None], :, ko] = kw.transpose(0, 2, 1)
+    vf[page[:, None], :, vo] = vw.transpose(0, 2, 1)
+    return kf.reshape(P, H, bs, d), vf.reshape(P, H, bs, d)
 
 
 def gather(k_pages, v_pages, block_table, b, h, L, kv_dtype="fp16",
            k_scale=None, v_scale=None):
     """Logical K, V of sequence b, kv head h, tokens 0..L-1, as float64 [L, d]."""
-    bs = k_pages.shape[2]
+    P, H, bs, d = k_pages.shape
+    X = chunk_elems(kv_dtype)
     t = np.arange(L)
     page = np.asarray(block_table, np.int64)[b, t // bs]
     slot = t % bs
-    k = k_pages[page, h, slot, :]
-    v = v_pages[page, h, :, slot]          # [L, d]
+    dims = np.arange(d)
+    kf = k_pages.reshape(P, H, bs * d)
+    vf = v_pages.reshape(P, H, bs * d)
+    k = kf[page[:, None], h, k_offset(slot[:, None], dims[None, :], d, X)]   # [L, d]
+    v = vf[page[:, None], h, v_offset(slot[:, None], dims[None, :], d)]
     if kv_dtype == "fp16":
         return k.astype(np.float64), v.astype(np.float64)
     return (fp8.decode(k) * np.float64(k_scale[h]),

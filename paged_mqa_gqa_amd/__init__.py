@@ -65,7 +65,7 @@ def load():
         "paged_decode_attn": (I, [D, P, P, P, P, P, F, P, P, P, P]),
         "paged_decode_attn_splitk_workspace_size": (Z, [D, I]),
         "paged_decode_attn_splitk": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P]),
-        "paged_decode_attn_splitk_reduce": (I, [D, I, P, Z, P, P]),
+        "paged_decode_attn_splitk_reduce": (I, [D, P, I, P, Z, P, P]),
         "paged_decode_attn_suggest_splits": (I, [D, I]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_version": (I, []),
@@ -117,7 +117,10 @@ def _need(t, name, dtype=None, ndim=None, cuda=True):
 
 
 def dims(num_seqs, num_q_heads, k_pages: torch.Tensor, block_table: torch.Tensor) -> PaDims:
-    """PaDims from the pool [P, Hkv, bs, d] and block table [B, max_blocks]."""
+    """PaDims from a pool allocation [P, Hkv, bs, d] and block table [B, max_blocks].
+
+    The bs * d values of one (page, head) are stored in the library's page
+    order (see include/paged_attn.h), not as a [bs, d] matrix."""
     P, Hkv, bs, d = k_pages.shape
     return PaDims(num_seqs, num_q_heads, Hkv, d, bs, P, block_table.shape[1],
                   _kv_dtype(k_pages))
@@ -161,8 +164,8 @@ def _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scal
     B, Hq, dq = q.shape
     d = dims(B, Hq, k_pages, block_table)
     P, Hkv, bs, hd = k_pages.shape
-    if v_pages.shape != (P, Hkv, hd, bs) or v_pages.dtype != k_pages.dtype:
-        raise ValueError("v_pages must be [P, Hkv, d, bs] with k_pages' dtype")
+    if v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
+        raise ValueError("v_pages must match k_pages' shape [P, Hkv, bs, d] and dtype")
     if dq != hd or block_table.shape[0] != B or context_lens.shape[0] != B:
         raise ValueError("inconsistent q / block_table / context_lens shapes")
     if d.kv_dtype == KV_FP8_E4M3FN:
@@ -206,26 +209,29 @@ def paged_decode_attn_splitk(q, k_pages, v_pages, block_table, context_lens, sca
     return workspace
 
 
-def paged_decode_attn_splitk_reduce(q_like, k_pages, block_table, num_splits, workspace,
-                                    out=None, stream=None):
+def paged_decode_attn_splitk_reduce(q_like, k_pages, block_table, context_lens,
+                                    num_splits, workspace, out=None, stream=None):
     """Merge pass; q_like gives [B, Hq, d]. Returns out fp16."""
     B, Hq, _ = q_like.shape
     d = dims(B, Hq, k_pages, block_table)
+    _need(context_lens, "context_lens", torch.int32, 1)
     if out is None:
         out = torch.empty(q_like.shape, dtype=torch.float16, device=q_like.device)
     _need(out, "out", torch.float16, 3)
     nbytes = workspace.numel() * workspace.element_size()
-    rc = load().paged_decode_attn_splitk_reduce(ctypes.byref(d), int(num_splits), _ptr(workspace),
-                                                nbytes, _ptr(out), _stream(stream))
+    rc = load().paged_decode_attn_splitk_reduce(ctypes.byref(d), _ptr(context_lens),
+                                                int(num_splits), _ptr(workspace), nbytes,
+                                                _ptr(out), _stream(stream))
     _check("paged_decode_attn_splitk_reduce", rc)
     return out
 
 
-def split_views(workspace, B, Hq, S, D):
-    """(o [B, Hq, S, D], lse [B, Hq, S]) float32 views of a split workspace."""
-    f = workspace.view(torch.float32)
+def split_views(workspace, B, Hq, Hkv, S, D):
+    """(o [B,Hq,S,D] f32, lse [B,Hq,S] f32, count [B,Hkv] i32) views of a workspace."""
     n = B * Hq * S
-    return f[:n * D].view(B, Hq, S, D), f[n * D:n * D + n].view(B, Hq, S)
+    f = workspace[:(n * D + n) * 4].view(torch.float32)
+    c = workspace[(n * D + n) * 4:(n * D + n) * 4 + B * Hkv * 4].view(torch.int32)
+    return f[:n * D].view(B, Hq, S, D), f[n * D:].view(B, Hq, S), c.view(B, Hkv)
 
 
 def suggest_splits(d: PaDims, max_context_len: int) -> int:

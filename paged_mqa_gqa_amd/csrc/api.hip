@@ -56,9 +56,26 @@ pa::AttnArgs make_args(const pa_dims* d, const void* q, const void* kp,
   return a;
 }
 
+// Workspace: o f32 [B, Hq, S, D], lse f32 [B, Hq, S], count i32 [B, Hkv].
 size_t ws_bytes(const pa_dims* d, int32_t S) {
   const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
-  return rows * (size_t)d->head_dim * sizeof(float) + rows * sizeof(float);
+  return rows * (size_t)d->head_dim * sizeof(float) + rows * sizeof(float) +
+         (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
+}
+
+struct WsViews {
+  float* o;
+  float* lse;
+  int32_t* count;
+};
+
+WsViews ws_views(const pa_dims* d, int32_t S, void* ws) {
+  const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
+  WsViews v;
+  v.o = static_cast<float*>(ws);
+  v.lse = v.o + rows * d->head_dim;
+  v.count = reinterpret_cast<int32_t*>(v.lse + rows);
+  return v;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -122,7 +139,7 @@ int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
                              context_lens, scale, k_scale, v_scale);
   a.out = static_cast<_Float16*>(out);
   a.S = 1;
-  a.split = 0;
+  a.mode = 0;
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
 }
@@ -155,49 +172,61 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
     return PA_ERR_WORKSPACE;
   pa::AttnArgs a = make_args(dims, q, k_pages, v_pages, block_table,
                              context_lens, scale, k_scale, v_scale);
-  const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads * num_splits;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_lse = a.ws_o + rows * dims->head_dim;
+  const WsViews v = ws_views(dims, num_splits, workspace);
+  a.ws_o = v.o;
+  a.ws_lse = v.lse;
+  a.ws_count = v.count;
   a.S = num_splits;
-  a.split = 1;
+  a.mode = num_splits == 1 ? 1 : 2;
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
 }
 
-int paged_decode_attn_splitk_reduce(const pa_dims* dims, int32_t num_splits,
-                                    const void* workspace,
+int paged_decode_attn_splitk_reduce(const pa_dims* dims,
+                                    const int32_t* context_lens,
+                                    int32_t num_splits, const void* workspace,
                                     size_t workspace_bytes, void* out,
                                     hipStream_t stream) {
   int rc = check_dims(dims);
   if (rc) return rc;
-  if (!out) return PA_ERR_NULL;
+  if (!out || !context_lens) return PA_ERR_NULL;
   if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
   if ((long long)dims->num_seqs * dims->num_q_heads > INT_MAX) return PA_ERR_SHAPE;
   if (dims->num_seqs == 0) return PA_OK;
   if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
     return PA_ERR_WORKSPACE;
   pa::ReduceArgs a{};
-  const size_t rows = (size_t)dims->num_seqs * dims->num_q_heads * num_splits;
-  a.ws_o = static_cast<const float*>(workspace);
-  a.ws_lse = a.ws_o + rows * dims->head_dim;
+  const WsViews v = ws_views(dims, num_splits, const_cast<void*>(workspace));
+  a.ws_o = v.o;
+  a.ws_lse = v.lse;
+  a.ws_count = v.count;
+  a.context_lens = context_lens;
   a.out = static_cast<_Float16*>(out);
-  a.rows = dims->num_seqs * dims->num_q_heads;
+  a.B = dims->num_seqs;
+  a.Hq = dims->num_q_heads;
+  a.Hkv = dims->num_kv_heads;
+  a.G = dims->num_q_heads / dims->num_kv_heads;
   a.S = num_splits;
+  a.cap = dims->max_blocks_per_seq * dims->block_size;
   return hip_status(pa::launch_reduce(a, dims->head_dim, stream));
 }
 
 int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
                                          int32_t max_context_len) {
   if (check_dims(dims) != PA_OK || max_context_len <= 0) return 1;
-  // aim for ~2048 workgroups (8 per compute unit on 256 CUs) while keeping
-  // every split at least 8 pages long
-  const long long wgs = (long long)dims->num_seqs * dims->num_kv_heads;
-  long long S = (2048 + wgs - 1) / (wgs > 0 ? wgs : 1);
-  const long long min_chunk = 8LL * dims->block_size;
-  const long long max_S = (max_context_len + min_chunk - 1) / min_chunk;
-  if (S > max_S) S = max_S;
-  if (S < 1) S = 1;
-  if (S > PA_MAX_SPLITS) S = PA_MAX_SPLITS;
+  // The split pass spreads the batch's 32-token tiles evenly over a
+  // persistent grid of W workgroups (512 for <= 16 q heads per kv head,
+  // else 256); the longest (sequence, kv head) then spans about
+  // n_max * W / T + 1 of them. Assuming the batch's mean context is at
+  // least 1/16 of the longest (T >= pairs * n_max / 16) gives the bound.
+  const long long W = dims->num_q_heads / dims->num_kv_heads <= 16 ? 512 : 256;
+  const long long tiles = (max_context_len + 31) / 32;
+  const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;
+  if (tiles <= 1 || pairs <= 0) return 1;
+  long long S = (16 * W + pairs - 1) / pairs + 1;
+  if (S > 64) S = 64;
+  if (S > tiles + 1) S = tiles + 1;
+  if (S < 2) S = 2;
   return (int32_t)S;
 }
 

@@ -6,8 +6,9 @@
 // Attention的专项优化支持", quantisation paragraph: K and V scaled apart).
 //
 // One thread handles two adjacent dimensions of one (token, kv head) row:
-// it reads 4 bytes of k_new and of v_new, writes them (or their two fp8
-// codes) into the K page row (contiguous) and the V page column (stride bs).
+// it reads 4 bytes of k_new and of v_new and writes them (or their two fp8
+// codes) at the positions the page layout gives them: both K values sit in
+// one 16-byte chunk; the two V values are 4 elements apart.
 #include "launch.h"
 #include "device_common.h"
 
@@ -33,14 +34,18 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
       a.k_new + (row * D + dp) * 2);
   const uint32_t vin = *reinterpret_cast<const uint32_t*>(
       a.v_new + (row * D + dp) * 2);
-  const long long tile = (long long)page * a.Hkv + h;   // (page, head) tile
+  // element offsets inside the (page, head) tile (16-token blocks)
+  constexpr int X = FP8 ? 16 : 8;                     // elements per 16 B
+  const int blk = slot >> 4, r = slot & 15;
+  const long long tile = ((long long)page * a.Hkv + h) * a.bs * D;
+  const long long koff = tile + ((blk * (D / X) + dp / X) * 16 + r) * X + dp % X;
+  const long long voff = tile + (((blk * (D / 16) + dp / 16) * 4 + (r >> 2)) * 16 +
+                                 dp % 16) * 4 + (r & 3);
   if constexpr (!FP8) {
-    uint8_t* kdst = a.k_pages + ((tile * a.bs + slot) * D + dp) * 2;
-    *reinterpret_cast<uint32_t*>(kdst) = kin;
-    uint16_t* vdst = reinterpret_cast<uint16_t*>(a.v_pages) +
-                     (tile * D + dp) * a.bs + slot;
+    *reinterpret_cast<uint32_t*>(a.k_pages + koff * 2) = kin;
+    uint16_t* vdst = reinterpret_cast<uint16_t*>(a.v_pages) + voff;
     vdst[0] = (uint16_t)(vin & 0xFFFFu);
-    vdst[a.bs] = (uint16_t)(vin >> 16);
+    vdst[4] = (uint16_t)(vin >> 16);
   } else {
     const float ks = a.k_scale[h];
     const float vs = a.v_scale[h];
@@ -52,11 +57,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
     const uint32_t k1 = f32_to_e4m3fn(h2f(kin >> 16) / ks);
     const uint32_t v0 = f32_to_e4m3fn(h2f(vin & 0xFFFFu) / vs);
     const uint32_t v1 = f32_to_e4m3fn(h2f(vin >> 16) / vs);
-    uint8_t* kdst = a.k_pages + (tile * a.bs + slot) * D + dp;
-    *reinterpret_cast<uint16_t*>(kdst) = (uint16_t)(k0 | (k1 << 8));
-    uint8_t* vdst = a.v_pages + (tile * D + dp) * a.bs + slot;
-    vdst[0] = (uint8_t)v0;
-    vdst[a.bs] = (uint8_t)v1;
+    *reinterpret_cast<uint16_t*>(a.k_pages + koff) = (uint16_t)(k0 | (k1 << 8));
+    a.v_pages[voff] = (uint8_t)v0;
+    a.v_pages[voff + 4] = (uint8_t)v1;
   }
 }
 

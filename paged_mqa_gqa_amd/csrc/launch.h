@@ -30,17 +30,20 @@ struct AttnArgs {
   _Float16* out;             // single pass: [B, Hq, D]
   float* ws_o;               // split pass: [B, Hq, S, D]
   float* ws_lse;             // split pass: [B, Hq, S]
+  int32_t* ws_count;         // split pass: [B, Hkv] partials per (b, h)
   float scale_log2;          // scale * log2(e)
   int B, Hq, Hkv, G, P, max_blocks, S;
-  int split;                 // 0: write out, 1: write ws_o / ws_lse
+  int mode;                  // 0: single pass -> out; 1: one split per
+                             // (b, h) -> slot 0; 2: stream-K split pass
 };
 
 struct ReduceArgs {
   const float* ws_o;
   const float* ws_lse;
+  const int32_t* ws_count;
+  const int32_t* context_lens;
   _Float16* out;
-  int rows;                  // B * Hq
-  int S;
+  int B, Hq, Hkv, G, S, cap;  // cap = max_blocks * block_size
 };
 
 hipError_t launch_kv_append(const KvAppendArgs& a, int D, bool fp8,

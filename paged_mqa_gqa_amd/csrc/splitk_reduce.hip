@@ -5,7 +5,9 @@
 //   out = sum_i e^{lse_i - M} o_i / sum_i e^{lse_i - M},  M = max_i lse_i,
 // with empty chunks (lse = -inf) weighing zero.
 //
-// One wave per (sequence, q head) row; each lane owns D/64 dimensions.
+// One wave per (sequence, q head) row; each lane owns D/64 dimensions. The
+// split pass records how many partials each (sequence, kv head) received;
+// a sequence with no tokens gets zeros.
 #include "launch.h"
 #include "device_common.h"
 
@@ -16,21 +18,30 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
   constexpr int kPer = D / 64;                // dims per lane (1 or 2)
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= a.rows) return;
+  if (row >= a.B * a.Hq) return;
+  const int b = row / a.Hq;
+  const int h = (row % a.Hq) / a.G;
+  int L = a.context_lens[b];
+  L = L < 0 ? 0 : (L > a.cap ? a.cap : L);
+  int n = 0;
+  if (L > 0) {
+    n = a.ws_count[(long long)b * a.Hkv + h];
+    n = n < 1 ? 1 : (n > a.S ? a.S : n);
+  }
   const float* lse = a.ws_lse + (long long)row * a.S;
   const float* o = a.ws_o + (long long)row * a.S * D;
 
   float M = -INFINITY;
-  for (int i = 0; i < a.S; ++i) M = fmaxf(M, lse[i]);
+  for (int i = 0; i < n; ++i) M = fmaxf(M, lse[i]);
   float acc[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
   float den = 0.0f;
   if (M != -INFINITY) {
-    for (int i = 0; i < a.S; ++i) {
+    for (int i = 0; i < n; ++i) {
       const float li = lse[i];
       if (li == -INFINITY) continue;           // wave-uniform
-      const float w = __expf(li - M);
+      const float w = __builtin_amdgcn_exp2f((li - M) * kLog2e);
       den += w;
       const float* oi = o + (long long)i * D + lane * kPer;
       if constexpr (kPer == 2) {
@@ -49,7 +60,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int D, hipStream_t stream) {
-  const unsigned grid = (unsigned)((a.rows + 3) / 4);
+  const unsigned grid = (unsigned)(((long long)a.B * a.Hq + 3) / 4);
   if (D == 64)
     hipLaunchKernelGGL((splitk_reduce_kernel<64>), grid, 256, 0, stream, a);
   else

@@ -97,7 +97,7 @@ def test_splitk_validation():
     lib = pa.load()
     d = good_dims()
     need = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 4)
-    assert need == 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4
+    assert need == 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4 + 2 * 2 * 4
     assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 0) == 0
     call = lambda S, ws, n: lib.paged_decode_attn_splitk(
         ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, S, ws, n, None)
@@ -105,11 +105,12 @@ def test_splitk_validation():
     assert call(1025, FAKE, 10 ** 9) == -4
     assert call(4, FAKE, need - 1) == -5
     assert call(4, None, need) == -5
-    red = lambda S, ws, n, out=FAKE: lib.paged_decode_attn_splitk_reduce(
-        ctypes.byref(d), S, ws, n, out, None)
+    red = lambda S, ws, n, out=FAKE, lens=FAKE: lib.paged_decode_attn_splitk_reduce(
+        ctypes.byref(d), lens, S, ws, n, out, None)
     assert red(4, FAKE, need - 4) == -5
     assert red(0, FAKE, need) == -4
     assert red(4, FAKE, need, None) == -1
+    assert red(4, FAKE, need, FAKE, None) == -1
 
 
 def test_kv_append_validation():
@@ -135,8 +136,10 @@ def test_status_strings_and_version():
 
 def test_suggest_splits():
     d = pa.PaDims(32, 32, 8, 128, 16, 5000, 256, pa.KV_FP16)
-    s = pa.suggest_splits(d, 4096)
-    assert 1 <= s <= 32
+    assert pa.suggest_splits(d, 4096) == 33        # 16*512/256 + 1
     d4 = pa.PaDims(4, 32, 8, 128, 64, 9000, 2048, pa.KV_FP16)
-    assert pa.suggest_splits(d4, 131072) >= 16
+    assert pa.suggest_splits(d4, 131072) == 64      # capped
     assert pa.suggest_splits(d4, 1) == 1
+    assert pa.suggest_splits(d4, 40) == 3           # two tiles -> at most 3
+    d3 = pa.PaDims(64, 96, 1, 128, 32, 20000, 256, pa.KV_FP16)
+    assert pa.suggest_splits(d3, 8192) == 64

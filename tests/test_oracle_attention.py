@@ -14,22 +14,37 @@ from tests.oracle_cases import contiguous_reference_sdpa, oracle_decode, oracle_
 from workloads import make, make_case
 
 
-def _scatter_by_hand(K, V, perm_pages, bs, num_pages):
-    """Test-side page fill: K/V [Hkv, L, d] into pools, one token at a time.
+def _tile_pos_k(t, i, d, X=8):
+    """Header layout, K: 16-token blocks, 16-byte chunks of X elements."""
+    blk, r = divmod(t, 16)
+    c, x = divmod(i, X)
+    return ((blk * (d // X) + c) * 16 + r) * X + x
 
-    Token t goes to page perm_pages[t // bs], slot t % bs, following the
-    documented layout (K [P, Hkv, bs, d], V [P, Hkv, d, bs]).
+
+def _tile_pos_v(t, i, d):
+    """Header layout, V: 16-token blocks, 16-dim groups, token quads."""
+    blk, r = divmod(t, 16)
+    jd, n = divmod(i, 16)
+    q4, e = divmod(r, 4)
+    return (((blk * (d // 16) + jd) * 4 + q4) * 16 + n) * 4 + e
+
+
+def _scatter_by_hand(K, V, perm_pages, bs, num_pages):
+    """Test-side page fill: K/V [Hkv, L, d] into pools, one value at a time.
+
+    Token t goes to page perm_pages[t // bs], slot t % bs, at the position
+    the library header documents for a (page, head) tile of bs * d values.
     """
     Hkv, L, d = K.shape
-    kp = np.full((num_pages, Hkv, bs, d), np.nan)
-    vp = np.full((num_pages, Hkv, d, bs), np.nan)
+    kp = np.full((num_pages, Hkv, bs * d), np.nan)
+    vp = np.full((num_pages, Hkv, bs * d), np.nan)
     for t in range(L):
         p, s = perm_pages[t // bs], t % bs
         for h in range(Hkv):
             for i in range(d):
-                kp[p, h, s, i] = K[h, t, i]
-                vp[p, h, i, s] = V[h, t, i]
-    return kp, vp
+                kp[p, h, _tile_pos_k(s, i, d)] = K[h, t, i]
+                vp[p, h, _tile_pos_v(s, i, d)] = V[h, t, i]
+    return kp.reshape(num_pages, Hkv, bs, d), vp.reshape(num_pages, Hkv, bs, d)
 
 
 def _one_seq(q, K, V, scale, bs, rng, extra=3):
@@ -49,7 +64,7 @@ def _rand(rng, *shape, std=1.0):
 
 
 @pytest.mark.parametrize("Hq,Hkv,d,bs,L", [
-    (4, 1, 64, 16, 17), (8, 2, 32, 16, 40), (6, 3, 16, 32, 70), (4, 4, 8, 64, 130),
+    (4, 1, 64, 16, 17), (8, 2, 32, 16, 40), (6, 3, 16, 32, 70), (4, 4, 16, 64, 130),
 ])
 def test_matches_torch_sdpa(Hq, Hkv, d, bs, L):
     rng = np.random.default_rng(L)
@@ -85,7 +100,7 @@ def test_uniform_scores_give_mean_of_v():
 
 def test_two_tokens_logistic_closed_form():
     rng = np.random.default_rng(4)
-    q = _rand(rng, 1, 8); K = _rand(rng, 1, 2, 8); V = _rand(rng, 1, 2, 8)
+    q = _rand(rng, 1, 16); K = _rand(rng, 1, 2, 16); V = _rand(rng, 1, 2, 16)
     scale = 0.7
     s0 = scale * float(q[0] @ K[0, 0]); s1 = scale * float(q[0] @ K[0, 1])
     sig = 1.0 / (1.0 + math.exp(-(s0 - s1)))
@@ -123,9 +138,9 @@ def test_paged_equals_contiguous_for_any_page_permutation():
     outs = [_one_seq(q, K, V, 0.25, 16, np.random.default_rng(s)) for s in range(6)]
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
-    # contiguous: one page holding all tokens in order
-    one = oracle.decode(q[None], K.transpose(1, 0, 2)[None].transpose(0, 2, 1, 3),
-                        V.transpose(0, 2, 1)[None], np.zeros((1, 1), np.int32),
+    # contiguous: one page of 80 slots holding all 75 tokens in order
+    kp, vp = _scatter_by_hand(K, V, [0], 80, 1)
+    one = oracle.decode(q[None], kp, vp, np.zeros((1, 1), np.int32),
                         np.array([75]), 0.25)[0]
     assert np.max(np.abs(one - outs[0])) < 1e-14
 
@@ -177,12 +192,13 @@ def test_fp8_path_matches_sdpa_on_dequantised_values():
         bt = w.block_table[b]
         # dequantise with torch's float8 type, gathering by hand
         Kd = np.zeros((2, L, 32)); Vd = np.zeros((2, L, 32))
+        kf = k.reshape(k.shape[0], 2, -1); vf = v.reshape(v.shape[0], 2, -1)
         for t in range(L):
             p, s = bt[t // 16], t % 16
             for h in range(2):
-                kc = torch.from_numpy(k[p, h, s].copy()).view(torch.float8_e4m3fn)
-                vc = torch.from_numpy(v[p, h, :, s].copy()).view(torch.float8_e4m3fn)
-                Kd[h, t] = kc.to(torch.float64).numpy() * float(ks[h])
-                Vd[h, t] = vc.to(torch.float64).numpy() * float(vs[h])
+                kc = np.array([kf[p, h, _tile_pos_k(s, i, 32, X=16)] for i in range(32)], np.uint8)
+                vc = np.array([vf[p, h, _tile_pos_v(s, i, 32)] for i in range(32)], np.uint8)
+                Kd[h, t] = torch.from_numpy(kc).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(ks[h])
+                Vd[h, t] = torch.from_numpy(vc).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(vs[h])
         ref = contiguous_reference_sdpa(w.q[b].astype(np.float64), Kd, Vd, w.scale)
         assert np.max(np.abs(out[b] - ref)) < 1e-13

@@ -7,6 +7,7 @@ import torch
 import oracle
 from oracle import fp8
 from tests.oracle_cases import oracle_pools
+from tests.test_oracle_attention import _tile_pos_k, _tile_pos_v
 from workloads import make_case
 
 
@@ -105,14 +106,20 @@ def _bytes(a):
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
 def test_append_writes_target_slots_only(kv_dtype):
     w, bk, bv, k2, v2, kn, vn, pos, ks, vs = _append_case(kv_dtype)
-    tk = np.zeros(bk.shape, bool); tv = np.zeros(bv.shape, bool)
+    P, H, bs, d = bk.shape
+    X = 8 if kv_dtype == "fp16" else 16
+    bkf, bvf = bk.reshape(P, H, -1), bv.reshape(P, H, -1)
+    k2f, v2f = k2.reshape(P, H, -1), v2.reshape(P, H, -1)
+    tk = np.zeros(bkf.shape, bool); tv = np.zeros(bvf.shape, bool)
     for b in range(3):
         p = w.block_table[b, pos[b] // 16]; s = pos[b] % 16
-        tk[p, :, s, :] = True; tv[p, :, :, s] = True
+        ko = [_tile_pos_k(s, i, d, X) for i in range(d)]
+        vo = [_tile_pos_v(s, i, d) for i in range(d)]
+        tk[p, :, ko] = True; tv[p, :, vo] = True
         for h in range(2):
             if kv_dtype == "fp16":
-                assert np.array_equal(_bytes(k2[p, h, s]), _bytes(kn[b, h]))
-                assert np.array_equal(_bytes(v2[p, h, :, s]), _bytes(vn[b, h]))
+                assert np.array_equal(_bytes(k2f[p, h, ko]), _bytes(kn[b, h]))
+                assert np.array_equal(_bytes(v2f[p, h, vo]), _bytes(vn[b, h]))
             else:   # torch's cast as the library reference; it does not
                     # saturate, so magnitudes >= 448 expect the +-448 code
                 yk = kn[b, h].astype(np.float32) / np.float32(ks[h])
@@ -121,11 +128,28 @@ def test_append_writes_target_slots_only(kv_dtype):
                                    torch.from_numpy(np.clip(y, -447, 447)).to(
                                        torch.float8_e4m3fn).view(torch.uint8).numpy()
                                    ).astype(np.uint8) for y in (yk, yv))
-                assert np.array_equal(k2[p, h, s], rk)
-                assert np.array_equal(v2[p, h, :, s], rv)
+                assert np.array_equal(k2f[p, h, ko], rk)
+                assert np.array_equal(v2f[p, h, vo], rv)
     # everything else unchanged, byte for byte
-    assert np.array_equal(_bytes(k2[~tk]), _bytes(bk[~tk]))
-    assert np.array_equal(_bytes(v2[~tv]), _bytes(bv[~tv]))
+    assert np.array_equal(_bytes(k2f[~tk]), _bytes(bkf[~tk]))
+    assert np.array_equal(_bytes(v2f[~tv]), _bytes(bvf[~tv]))
+
+
+def test_layout_offsets_are_a_bijection_of_the_tile():
+    for bs in (16, 32, 64):
+        for d in (64, 128):
+            for X in (8, 16):
+                ko = sorted(_tile_pos_k(t, i, d, X) for t in range(bs) for i in range(d))
+                assert ko == list(range(bs * d))
+            vo = sorted(_tile_pos_v(t, i, d) for t in range(bs) for i in range(d))
+            assert vo == list(range(bs * d))
+    # and the oracle's offsets agree with the hand-written ones
+    t = np.arange(64)[:, None]; i = np.arange(128)[None, :]
+    from oracle.paged import k_offset, v_offset
+    assert np.array_equal(k_offset(t, i, 128, 8),
+                          [[_tile_pos_k(a, b, 128, 8) for b in range(128)] for a in range(64)])
+    assert np.array_equal(v_offset(t, i, 128),
+                          [[_tile_pos_v(a, b, 128) for b in range(128)] for a in range(64)])
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])

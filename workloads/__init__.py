@@ -76,11 +76,11 @@ CONFIGS = {
     # Llama-style GQA layer: batch 32, 32 q / 8 kv heads, d 128, pages of 16,
     # lengths uniform on [512, 4096].
     "gqa_llama": Config("gqa_llama", 32, 32, 8, 128, 16, "fp16", 1.0,
-                        ("uniform", 512, 4096), 4096, 4, seed=1002),
+                        ("uniform", 512, 4096), 4096, 16, seed=1002),
     # Wide MQA: batch 64, 96 q / 1 kv head, d 128, pages of 32, 8192 each,
     # values N(0, 0.5) (standard deviation 0.5).
     "wide_mqa": Config("wide_mqa", 64, 96, 1, 128, 32, "fp16", 0.5,
-                       ("const", 8192), 8192, 4, seed=1003),
+                       ("const", 8192), 8192, 8, seed=1003),
     # Long-context split-K: batch 4, 32 q / 8 kv heads, d 128, pages of 64,
     # 131072 tokens each, 64 splits merged by log-sum-exp.
     "long_splitk": Config("long_splitk", 4, 32, 8, 128, 64, "fp16", 1.0,
@@ -89,7 +89,7 @@ CONFIGS = {
     # pages of 16, lengths log-normal (median 1024, sigma 1) clipped to
     # [1, 32768], per-kv-head fp32 scales, one append per sequence.
     "mixed_fp8": Config("mixed_fp8", 256, 64, 8, 128, 16, "fp8_e4m3fn", 1.0,
-                        ("lognormal", 1024, 1.0, 1, 32768), 32768, 8,
+                        ("lognormal", 1024, 1.0, 1, 32768), 32768, 16,
                         seed=1005),
 }
 

@@ -16,8 +16,7 @@ from . import Workload
 
 def _nan_pools(w: Workload, device):
     cfg = w.cfg
-    shape_k = (w.num_pages, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
-    shape_v = (w.num_pages, cfg.num_kv_heads, cfg.head_dim, cfg.block_size)
+    shape_k = shape_v = (w.num_pages, cfg.num_kv_heads, cfg.block_size, cfg.head_dim)
     if cfg.kv_dtype == "fp16":
         k = torch.full(shape_k, float("nan"), dtype=torch.float16, device=device)
         v = torch.full(shape_v, float("nan"), dtype=torch.float16, device=device)

@@ -71,18 +71,17 @@ def measured_traffic(workload: str):
         return None
 
 
-def attention_algorithmic_bytes(w, S: int) -> int:
-    """Bytes the attention pass must move at minimum: K/V of every attended
-    token, q, the block-table entries of those tokens, the context lengths,
-    and its output (fp16 out for one split, fp32 o + lse partials otherwise)."""
+def attention_algorithmic_bytes(w) -> int:
+    """Bytes decode attention must move at minimum: K/V of every attended
+    token, q, the block-table entries of those tokens, the context lengths
+    and the fp16 output (split partials are this implementation's overhead,
+    not counted)."""
     cfg = w.cfg
     L = w.context_lens.astype("int64")
     nblk = -(-L // cfg.block_size)
     qb = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 2
-    out = (cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 2 if S == 1 else
-           cfg.num_seqs * cfg.num_q_heads * S * (cfg.head_dim + 1) * 4)
-    return int(w.kv_bytes() + qb + int(nblk.sum()) * 4 * cfg.num_kv_heads
-               + cfg.num_seqs * 4 + out)
+    return int(w.kv_bytes() + 2 * qb + int(nblk.sum()) * 4 * cfg.num_kv_heads
+               + cfg.num_seqs * 4)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -154,8 +153,7 @@ def main():
                                           for _ in range(R - 1)]
     stream = torch.cuda.Stream()     # the stream every kernel goes to
     d = pa.dims(cfg.num_seqs, cfg.num_q_heads, dw.k_pages, dw.block_table)
-    ws = torch.empty(max(pa.splitk_workspace_size(d, S), 1), dtype=torch.uint8,
-                     device="cuda")
+    ws = pa.splitk_workspace(dw.q, dw.k_pages, dw.block_table, S)
     out = torch.empty_like(dw.q)
     torch.cuda.synchronize()
 
@@ -171,13 +169,12 @@ def main():
             if ev is not None:
                 ev[1].record(stream)
         else:
-            pa.paged_decode_attn_splitk(dw.q, kp, vp, dw.block_table, dw.context_lens,
-                                        dw.scale, S, dw.k_scale, dw.v_scale,
-                                        workspace=ws, stream=stream)
+            pa.paged_decode_attn_splitk_merged(dw.q, kp, vp, dw.block_table,
+                                               dw.context_lens, dw.scale, S, ws,
+                                               dw.k_scale, dw.v_scale, out=out,
+                                               stream=stream)
             if ev is not None:
                 ev[1].record(stream)
-            pa.paged_decode_attn_splitk_reduce(dw.q, kp, dw.block_table, dw.context_lens, S, ws,
-                                               out=out, stream=stream)
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
@@ -199,7 +196,7 @@ def main():
     attn_us = [a.elapsed_time(b) * 1e3 for a, b in events]
     attn_avg_us = float(np.mean(attn_us))
     value = kvb / (ms_step * 1e-3) / 1e9
-    alg = attention_algorithmic_bytes(w, S)
+    alg = attention_algorithmic_bytes(w)
     achieved = alg / (attn_avg_us * 1e-6) / 1e9
     traffic = measured_traffic(cfg.name)
 
@@ -226,7 +223,7 @@ def main():
             "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "context_tokens": int(w.context_lens.sum()), "splits": S,
             "pool_replicas": R, "step": "kv_append + attention" +
-            (" (single pass)" if S == 1 else " (split pass + merge)"),
+            (" (single pass)" if S == 1 else " (split pass with in-kernel merge)"),
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "us_per_step": round(ms_step * 1e3, 2),
@@ -237,7 +234,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "decode_attn_kernel" + (" (single pass)" if S == 1 else " (split pass)"),
+            "kernel": ("decode_attn_kernel (single pass)" if S == 1 else
+                       "decode_attn_streamk_kernel (split pass, merged)"),
             "algorithmic_bytes_per_launch": alg,
         },
         "cpu_baseline": cpu,

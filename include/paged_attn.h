@@ -48,14 +48,16 @@
  *   context_lens    [B]                   int32 tokens per sequence
  *   k_scale,v_scale [Hkv]                 fp32, fp8 caches only (else NULL)
  * Inside a tile, slot t (0 <= t < bs) and dimension i (0 <= i < d) sit at
- * element offset, with blk = t / 16, r = t % 16 and X = 16 bytes / element
- * size (8 for fp16, 16 for fp8):
- *   K:  ((blk * (d / X) + i / X) * 16 + r) * X + i % X
- *   V:  (((blk * (d / 16) + i / 16) * 4 + r / 4) * 16 + i % 16) * 4 + r % 4
+ * element offset, with blk = t / 16, r = t % 16, rho(r) = r with its bits
+ * 2 and 3 swapped, and X = 16 bytes / element size (8 for fp16, 16 for fp8):
+ *   K:  ((blk * (d / X) + i / X) * 16 + rho(r)) * X + i % X
+ *   V:  (((blk * (d / 16) + i / 16) * 2 + r / 8) * 16 + i % 16) * 8 + r % 8
  * i.e. each 16-token block stores K as 16-byte chunks of one token's row,
- * chunk-major, and V as runs of 4 tokens of one dimension; this is the
- * order in which the kernels' matrix-core operands are loaded, so every
- * wave-wide load is one contiguous run. A page pool may be allocated as
+ * chunk-major, with slots 0-3, 8-11 in the first 8 rows and 4-7, 12-15 in
+ * the last 8; and V as runs of 8 tokens of one dimension. This is the order
+ * in which the kernels' matrix-core operands are loaded: a lane's V operand
+ * is one 16-byte (fp16) or 8-byte (fp8) run and every wave-wide load reads
+ * whole 128-byte lines. A page pool may be allocated as
  * [P, Hkv, bs, d] (the binding does), but its last two axes are storage, not
  * a [token, dim] matrix. Caches are written through kv_append.
  * fp8 caches hold OCP E4M3FN codes (1 byte, max 448, no infinities); the
@@ -150,11 +152,15 @@ int paged_decode_attn(const pa_dims* dims, const void* q,
                       void* out, hipStream_t stream);
 
 /*
- * Workspace bytes needed by paged_decode_attn_splitk for num_splits partial
- * slots per (sequence, q head). Layout, densely packed in this order:
+ * Workspace bytes needed by paged_decode_attn_splitk and
+ * paged_decode_attn_splitk_merged for num_splits partial slots per
+ * (sequence, q head). Layout, densely packed in this order:
  *   o     float32 [B, Hq, S, d]   normalised partial outputs
  *   lse   float32 [B, Hq, S]      natural-log sum of exp(scores) per partial
  *   count int32   [B, Hkv]        partials written for (sequence, kv head)
+ *   sem   int32   [B, Hkv]        arrival counters of the merged call: must
+ *                                 be zero before its first use; every
+ *                                 completed merged call leaves them zero
  * Returns 0 for invalid dims or num_splits.
  */
 size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
@@ -201,6 +207,30 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
 int paged_decode_attn_splitk_reduce(const pa_dims* dims,
                                     const int32_t* context_lens,
                                     int32_t num_splits, const void* workspace,
+                                    size_t workspace_bytes, void* out,
+                                    hipStream_t stream);
+
+/*
+ * paged_decode_attn_splitk_merged — split decode attention in one launch.
+ *
+ * Same split as paged_decode_attn_splitk (ranges of the batch's tiles over
+ * a persistent grid, at most num_splits per (sequence, kv head)), with the
+ * log-sum-exp merge done in the same kernel: a (sequence, kv head) covered
+ * by one workgroup is normalised and written straight to `out`; otherwise
+ * each of its workgroups writes its partial to the workspace and counts its
+ * arrival on sem[b, h] (device-scope atomic after a device-scope fence),
+ * and the last to arrive merges the partials into `out` and resets
+ * sem[b, h] to zero. out [B, Hq, d] fp16 is the same result as
+ * paged_decode_attn up to rounding; sequences with L = 0 get zeros.
+ * Two merged calls that share one workspace must not run concurrently.
+ * num_splits == 1 runs paged_decode_attn (workspace unused).
+ */
+int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
+                                    const void* k_pages, const void* v_pages,
+                                    const int32_t* block_table,
+                                    const int32_t* context_lens, float scale,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t num_splits, void* workspace,
                                     size_t workspace_bytes, void* out,
                                     hipStream_t stream);
 

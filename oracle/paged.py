@@ -9,10 +9,10 @@ pages give no layout; the library's header fixes it and this file follows it.
 Pools are arrays [P, Hkv, bs, d] (the allocation shape); the bs * d
 elements of one (page, head) tile are stored in the order below, in units
 of 16-token blocks (blk = t // 16, r = t % 16; X = elements per 16 bytes:
-8 for fp16, 16 for fp8):
+8 for fp16, 16 for fp8; rho(r) = r with its bits 2 and 3 swapped):
 
-  K element (t, i):  ((blk * (d / X) + i // X) * 16 + r) * X + i % X
-  V element (t, i):  (((blk * (d / 16) + i // 16) * 4 + r // 4) * 16 + i % 16) * 4 + r % 4
+  K element (t, i):  ((blk * (d / X) + i // X) * 16 + rho(r)) * X + i % X
+  V element (t, i):  (((blk * (d / 16) + i // 16) * 2 + r // 8) * 16 + i % 16) * 8 + r % 8
 
 Token t of sequence b lives in page block_table[b, t // bs], slot t % bs.
 Element type is float16 or the uint8 code of fp8 e4m3fn; for fp8 each kv head
@@ -29,17 +29,24 @@ def chunk_elems(kv_dtype) -> int:
     return 8 if kv_dtype == "fp16" else 16
 
 
+def row_order(r):
+    """Storage row of slot r (0..15) inside a 16-token K block: the quads
+    r = 4..7 and 8..11 trade places (bits 2 and 3 of r swapped)."""
+    r = np.asarray(r)
+    return (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1)
+
+
 def k_offset(t, i, d, X):
     """Element offset of K (slot t, dim i) inside a (page, head) tile."""
     t = np.asarray(t); i = np.asarray(i)
-    return ((t // 16 * (d // X) + i // X) * 16 + t % 16) * X + i % X
+    return ((t // 16 * (d // X) + i // X) * 16 + row_order(t % 16)) * X + i % X
 
 
 def v_offset(t, i, d):
     """Element offset of V (slot t, dim i) inside a (page, head) tile."""
     t = np.asarray(t); i = np.asarray(i)
     r = t % 16
-    return (((t // 16 * (d // 16) + i // 16) * 4 + r // 4) * 16 + i % 16) * 4 + r % 4
+    return (((t // 16 * (d // 16) + i // 16) * 2 + r // 8) * 16 + i % 16) * 8 + r % 8
 
 
 def empty_pools(num_pages, num_kv_heads, block_size, head_dim, kv_dtype):

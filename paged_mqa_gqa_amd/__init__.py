@@ -19,7 +19,8 @@ import torch
 __all__ = [
     "PaDims", "PagedAttnError", "KV_FP16", "KV_FP8_E4M3FN", "library_path",
     "load", "dims", "kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
-    "paged_decode_attn_splitk_reduce", "splitk_workspace_size",
+    "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
+    "splitk_workspace", "splitk_workspace_size",
     "suggest_splits", "status_string", "version",
 ]
 
@@ -66,6 +67,7 @@ def load():
         "paged_decode_attn_splitk_workspace_size": (Z, [D, I]),
         "paged_decode_attn_splitk": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P]),
         "paged_decode_attn_splitk_reduce": (I, [D, P, I, P, Z, P, P]),
+        "paged_decode_attn_splitk_merged": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
         "paged_decode_attn_suggest_splits": (I, [D, I]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_version": (I, []),
@@ -191,14 +193,20 @@ def splitk_workspace_size(d: PaDims, num_splits: int) -> int:
     return int(load().paged_decode_attn_splitk_workspace_size(ctypes.byref(d), num_splits))
 
 
+def splitk_workspace(q, k_pages, block_table, num_splits):
+    """A zero-filled workspace for the split calls (uint8 device tensor)."""
+    d = dims(q.shape[0], q.shape[1], k_pages, block_table)
+    return torch.zeros(max(splitk_workspace_size(d, num_splits), 1), dtype=torch.uint8,
+                       device=q.device)
+
+
 def paged_decode_attn_splitk(q, k_pages, v_pages, block_table, context_lens, scale,
                              num_splits, k_scale=None, v_scale=None, workspace=None,
                              stream=None):
     """Split pass; returns the workspace (uint8 tensor holding o then lse)."""
     d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
-    need = splitk_workspace_size(d, num_splits)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        workspace = splitk_workspace(q, k_pages, block_table, num_splits)
     _need(workspace, "workspace")
     nbytes = workspace.numel() * workspace.element_size()
     rc = load().paged_decode_attn_splitk(ctypes.byref(d), _ptr(q), _ptr(k_pages), _ptr(v_pages),
@@ -223,6 +231,27 @@ def paged_decode_attn_splitk_reduce(q_like, k_pages, block_table, context_lens,
                                                 int(num_splits), _ptr(workspace), nbytes,
                                                 _ptr(out), _stream(stream))
     _check("paged_decode_attn_splitk_reduce", rc)
+    return out
+
+
+def paged_decode_attn_splitk_merged(q, k_pages, v_pages, block_table, context_lens, scale,
+                                    num_splits, workspace, k_scale=None, v_scale=None,
+                                    out=None, stream=None):
+    """Split pass with the merge in the same launch; returns out [B, Hq, d] fp16.
+
+    `workspace` must come from splitk_workspace() (its counters start at zero)
+    and must not be shared by two merged calls running at the same time."""
+    d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, 3)
+    _need(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load().paged_decode_attn_splitk_merged(
+        ctypes.byref(d), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+        _ptr(context_lens), float(scale), _ptr(k_scale), _ptr(v_scale), int(num_splits),
+        _ptr(workspace), nbytes, _ptr(out), _stream(stream))
+    _check("paged_decode_attn_splitk_merged", rc)
     return out
 
 

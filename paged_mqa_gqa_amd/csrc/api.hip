@@ -56,17 +56,19 @@ pa::AttnArgs make_args(const pa_dims* d, const void* q, const void* kp,
   return a;
 }
 
-// Workspace: o f32 [B, Hq, S, D], lse f32 [B, Hq, S], count i32 [B, Hkv].
+// Workspace: o f32 [B, Hq, S, D], lse f32 [B, Hq, S], count i32 [B, Hkv],
+// sem i32 [B, Hkv].
 size_t ws_bytes(const pa_dims* d, int32_t S) {
   const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
   return rows * (size_t)d->head_dim * sizeof(float) + rows * sizeof(float) +
-         (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
+         2 * (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
 }
 
 struct WsViews {
   float* o;
   float* lse;
   int32_t* count;
+  int32_t* sem;
 };
 
 WsViews ws_views(const pa_dims* d, int32_t S, void* ws) {
@@ -75,6 +77,7 @@ WsViews ws_views(const pa_dims* d, int32_t S, void* ws) {
   v.o = static_cast<float*>(ws);
   v.lse = v.o + rows * d->head_dim;
   v.count = reinterpret_cast<int32_t*>(v.lse + rows);
+  v.sem = v.count + (size_t)d->num_seqs * d->num_kv_heads;
   return v;
 }
 
@@ -176,8 +179,46 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
   a.ws_o = v.o;
   a.ws_lse = v.lse;
   a.ws_count = v.count;
+  a.ws_sem = v.sem;
   a.S = num_splits;
   a.mode = num_splits == 1 ? 1 : 2;
+  return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
+                                    dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+}
+
+int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
+                                    const void* k_pages, const void* v_pages,
+                                    const int32_t* block_table,
+                                    const int32_t* context_lens, float scale,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, void* out,
+                                    hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
+    return PA_ERR_NULL;
+  rc = check_scales(dims, k_scale, v_scale);
+  if (rc) return rc;
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
+  if ((long long)dims->num_seqs * dims->num_kv_heads * num_splits > INT_MAX)
+    return PA_ERR_SHAPE;
+  if (dims->num_seqs == 0) return PA_OK;
+  if (num_splits == 1)   // one range per (sequence, kv head): the single pass
+    return paged_decode_attn(dims, q, k_pages, v_pages, block_table,
+                             context_lens, scale, k_scale, v_scale, out, stream);
+  if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
+    return PA_ERR_WORKSPACE;
+  pa::AttnArgs a = make_args(dims, q, k_pages, v_pages, block_table,
+                             context_lens, scale, k_scale, v_scale);
+  const WsViews v = ws_views(dims, num_splits, workspace);
+  a.ws_o = v.o;
+  a.ws_lse = v.lse;
+  a.ws_count = v.count;
+  a.ws_sem = v.sem;
+  a.out = static_cast<_Float16*>(out);
+  a.S = num_splits;
+  a.mode = 3;
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
 }

@@ -9,35 +9,39 @@
 // long-context decode in roadmap row FlashDecoding).
 //
 // Design (MI355X / gfx950):
-//  * A workgroup's waves are NWH groups of head blocks (16 q heads per MFMA
-//    block, NH blocks per wave) times TW token-parallel waves. Every wave
-//    streams its own 32-token tiles straight from HBM into MFMA operand
-//    registers, the next tile's loads in flight while the current tile is
-//    computed. The page layout stores each 16-token block in operand order,
-//    so every wave-wide load reads one contiguous run (1 KB per K load,
-//    512 B per fp16 V load) and the L1 sees full 64-byte requests.
-//  * QK^T: a 16-token K block as the A operand (16 tokens x 32 dims), the
-//    group's q heads as B (32 dims x 16 heads). The 16x16 result holds, per
-//    lane, scores of one head for 4 tokens; the two blocks of a tile give
-//    the 8 tokens that the P.V product needs in the same lane, so P never
-//    leaves registers.
+//  * Work unit: a 32-token tile of one (sequence, kv head) for the 16-head
+//    blocks of the group a wave owns (NH blocks per wave; NWH waves share a
+//    tile stream when the group has more heads). Tiles stream straight from
+//    HBM into MFMA operand registers, the next tile's loads in flight while
+//    the current tile is computed. The page layout stores each 16-token
+//    block in operand order, so every wave-wide load reads whole 128-byte
+//    lines and a lane's V operand is one 16-byte (fp8: 8-byte) run.
+//  * QK^T: 16 tokens of the tile as the A operand (16 tokens x 32 dims),
+//    the group's q heads as B (32 dims x 16 heads). The 16x16 result holds,
+//    per lane, scores of one head for 4 tokens; the two token halves of a
+//    tile are picked so that a lane ends up with 8 consecutive tokens, the
+//    8 that the P.V product needs in the same lane, so P never leaves
+//    registers.
 //  * Online softmax in base 2 (scale * log2 e folded into the scores): the
 //    running max per head is reduced across the four 16-lane groups, the
 //    running sum stays per lane until a flush.
-//  * P.V: P (16 heads x 32 tokens, fp16) as A, V page columns (32 tokens x
-//    16 dims) as B, accumulated in fp32.
-//  * Page ids of a token range are staged in LDS (chunks of kMaxPages) and
-//    clamped into the pool; masked tail tokens re-read a valid row and are
-//    zeroed by select, so NaN in unused slots never leaks.
+//  * P.V: P (16 heads x 32 tokens, fp16) as A, V (32 tokens x 16 dims) as
+//    B, accumulated in fp32.
+//  * Page ids are clamped into the pool; tokens past the end re-read a
+//    valid block and are masked by select, so NaN in unused slots never
+//    leaks.
 //  * fp8 e4m3fn K/V are expanded to fp16 in registers by bit placement
 //    (value * 2^-8, exact); 2^8 and the per-head scales fold into the score
 //    scale and the final output scale.
-//  * Two schedules. Single pass: one workgroup per (sequence, kv head).
-//    Split pass: a persistent grid; the tiles of all (sequence, kv head)
-//    contexts, laid end to end, are cut into equal contiguous shares, one
-//    per workgroup (the stream-K decomposition), so ragged batches balance
-//    exactly; every (sequence, kv head) segment a workgroup covers becomes
-//    one log-sum-exp partial, merged by the separate reduce kernel.
+//  * Two schedules. Single pass: one workgroup per (sequence, kv head), its
+//    token-parallel waves merged through LDS. Split pass (stream-K): every
+//    wave (or head-parallel wave group) is a worker; the tiles of all
+//    (sequence, kv head) contexts, laid end to end, are cut into equal
+//    contiguous shares, one per worker, so ragged batches balance exactly.
+//    A worker streams its share as one pipeline across (sequence, kv head)
+//    boundaries (no barriers), and each (sequence, kv head) segment it
+//    covers becomes one log-sum-exp partial, merged by the reduce kernel or,
+//    in the merged call, by the last of its workers to finish.
 #include "launch.h"
 #include "device_common.h"
 
@@ -46,20 +50,21 @@
 namespace pa {
 
 constexpr int kTile = 32;       // tokens per tile
-constexpr int kMaxPages = 512;  // page ids staged in LDS per chunk
+constexpr int kMaxPages = 512;  // page ids staged in LDS per chunk (single pass)
 
 template <int D, int BS, bool FP8>
 struct Geo {
   static constexpr int kEsz = FP8 ? 1 : 2;
-  static constexpr int kRowBytes = D * kEsz;          // one K row
+  static constexpr int kRowBytes = D * kEsz;          // one token row
+  static constexpr int kBlockBytes = 16 * kRowBytes;  // one 16-token block
   static constexpr int kPageBytes = BS * D * kEsz;    // one (page, head) tile
   static constexpr int kQkMfma = D / 32;              // per 16-token block
-  static constexpr int kKLoads = kRowBytes / 64;      // 16 B loads per K row
+  static constexpr int kKLoads = kRowBytes / 64;      // 16 B loads per block
   static constexpr int kPvMfma = D / 16;              // per 32-token tile
 };
 
 // First dimension of the 8 K-slots that lane group g (= lane / 16) holds in
-// QK MFMA number jj. fp16: a 16 B K load covers one MFMA; fp8: a 16 B load
+// QK MFMA number jj. fp16: a 16 B K chunk covers one MFMA; fp8: a 16 B chunk
 // covers 16 dims, i.e. two MFMAs.
 template <bool FP8>
 __device__ __forceinline__ int kslot_dim(int jj, int g) {
@@ -69,53 +74,63 @@ __device__ __forceinline__ int kslot_dim(int jj, int g) {
 template <int D, int BS, bool FP8>
 struct TileRegs {
   using G = Geo<D, BS, FP8>;
-  // V of one 16-token block: 4 tokens of one dimension per lane
-  using VT = typename std::conditional<FP8, uint32_t, u32x2>::type;
-  u32x4 k[2][G::kKLoads];      // [16-token block][16 B chunk group]
-  VT v[2][G::kPvMfma];         // [16-token block][16-dim group]
+  // V operand of one 16-dim group: the lane's 8 tokens of one dimension,
+  // one contiguous run in the page
+  using VT = typename std::conditional<FP8, u32x2, u32x4>::type;
+  u32x4 k[2][G::kKLoads];      // [QK MFMA m][chunk group]
+  VT v[G::kPvMfma];            // [16-dim group]
 };
 
-template <int NH, int NWH, int TW, int D>
-struct SharedMem {
-  static constexpr int kHeads = NWH * NH * 16;
-  int pages[kMaxPages];
-  float m[TW][kHeads];
-  float l[TW][kHeads];
-  float acc[TW > 1 ? TW - 1 : 1][kHeads][D];
-  int scan[256];
-  int loc[4];
-};
+// Issue the loads of one tile whose two 16-token blocks start at byte
+// offsets off0 / off1 of the K and V pools (head offset included).
+//
+// Token order inside the tile: QK MFMA m (0, 1) takes as its 16 A rows the
+// tokens 8 * (R / 4) + 4 * m + R % 4 (R = 0..15), i.e. rows 0..7 from block
+// 0 and 8..15 from block 1; its result gives lane group lg the tokens
+// 8 * lg + 4 * m + 0..3, so a lane's 8 probabilities are the tokens
+// 8 * lg + 0..7 of the tile, all in block lg / 2: the V operand that P.V
+// needs is one run of 8 tokens. In a block's K storage rows 8 * m + 0..7
+// hold exactly MFMA m's tokens of that block.
+template <int D, int BS, bool FP8>
+__device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
+                                          const uint8_t* kbase,
+                                          const uint8_t* vbase, long long off0,
+                                          long long off1, int lane) {
+  using Gm = Geo<D, BS, FP8>;
+  const int R = lane & 15, lg = lane >> 4;
+  const uint8_t* kb = kbase + (R < 8 ? off0 : off1) + (lg * 16 + (R & 7)) * 16;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int jl = 0; jl < Gm::kKLoads; ++jl)
+      t.k[m][jl] = *reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl);
+  const uint8_t* vb = vbase + (lg < 2 ? off0 : off1) + ((lg & 1) * 16 + R) * 8 * Gm::kEsz;
+#pragma unroll
+  for (int jd = 0; jd < Gm::kPvMfma; ++jd)
+    t.v[jd] = *reinterpret_cast<const typename TileRegs<D, BS, FP8>::VT*>(
+        vb + jd * 256 * Gm::kEsz);
+}
 
-template <int D, int BS, bool FP8, int NH, int NWH, int TW>
-struct Decoder {
+// Attention state of one wave for NH blocks of 16 q heads of one (sequence,
+// kv head), and the math of one tile.
+template <int D, int BS, bool FP8, int NH>
+struct HeadState {
   using Gm = Geo<D, BS, FP8>;
   using Tile = TileRegs<D, BS, FP8>;
-  using Smem = SharedMem<NH, NWH, TW, D>;
-
-  const AttnArgs& a;
-  Smem& sm;
-  int lane, wave, hw, tw, mrow, lg;
-  float sl, oscale;
   half8 qop[NH][Gm::kQkMfma];
   float mrun[NH], lrun[NH];
   f32x4 acc[NH][Gm::kPvMfma];
+  float sl, oscale;
 
-  __device__ __forceinline__ Decoder(const AttnArgs& args, Smem& s) : a(args), sm(s) {
-    lane = threadIdx.x & 63;
-    wave = threadIdx.x >> 6;
-    hw = wave % NWH;
-    tw = wave / NWH;
-    mrow = lane & 15;
-    lg = lane >> 4;
-  }
-
-  // q rows of kv group h of sequence b as B operands; softmax state reset.
-  __device__ __forceinline__ void begin(int b, int h) {
+  // q rows of heads (hw*NH + hb)*16 + lane%16 of group h of sequence b as
+  // B operands (zeros past the group), softmax state reset.
+  __device__ __forceinline__ void begin(const AttnArgs& a, int b, int h, int hw,
+                                        int mrow, int lg) {
     sl = a.scale_log2;
     oscale = 1.0f;
     if constexpr (FP8) {
-      sl *= a.k_scale[h] * 256.0f;
-      oscale = a.v_scale[h] * 256.0f;
+      sl *= load_uniform(a.k_scale + h) * 256.0f;
+      oscale = load_uniform(a.v_scale + h) * 256.0f;
     }
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
@@ -135,125 +150,53 @@ struct Decoder {
     }
   }
 
-  // Attend to tokens [start, end) of (b, h). Every wave of the workgroup
-  // must call this with the same arguments (it synchronises the group).
-  __device__ __forceinline__ void run(int b, int h, int start, int end) {
-    const uint8_t* kbase = a.k_pages + (long long)h * Gm::kPageBytes;
-    const uint8_t* vbase = a.v_pages + (long long)h * Gm::kPageBytes;
-    const long long page_stride = (long long)a.Hkv * Gm::kPageBytes;
-    const int* bt_row = a.block_table + (long long)b * a.max_blocks;
-
-    for (int cs = start; cs < end; cs += kMaxPages * BS) {
-      const int ce = min(end, cs + kMaxPages * BS);
-      const int p0 = cs / BS;
-      const int np = (ce - 1) / BS - p0 + 1;
-      __syncthreads();   // previous chunk's ids (and flush buffers) are free
-      for (int i = threadIdx.x; i < np; i += blockDim.x) {
-        int p = bt_row[p0 + i];
-        sm.pages[i] = p < 0 ? 0 : (p >= a.P ? a.P - 1 : p);
-      }
-      __syncthreads();
-      const int ntiles = (ce - cs + kTile - 1) / kTile;
-
-      // Issue the loads of tile k (two 16-token blocks). A block that lies
-      // wholly past the end re-reads the last block that has tokens (in
-      // bounds; its values are masked).
-      auto load_tile = [&](Tile& t, int k) {
-        const int ts = cs + k * kTile;
-        const int last_blk = (ce - 1) & ~15;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int tb = min(ts + 16 * r, last_blk);
-          const int page = sm.pages[tb / BS - p0];
-          const long long off = page * page_stride + (tb % BS) * Gm::kRowBytes;
-          const uint8_t* kb = kbase + off + lane * 16;
-#pragma unroll
-          for (int jl = 0; jl < Gm::kKLoads; ++jl)
-            t.k[r][jl] = *reinterpret_cast<const u32x4*>(kb + 1024 * jl);
-          const uint8_t* vb = vbase + off + lane * 4 * Gm::kEsz;
-#pragma unroll
-          for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-            t.v[r][jd] = *reinterpret_cast<const typename Tile::VT*>(
-                vb + jd * 256 * Gm::kEsz);
-        }
-      };
-
-      // Two register tiles in flight. The next tile's loads are issued on
-      // every iteration, unconditionally: past the last tile they re-read
-      // the current tile (lines already in L2) into the idle buffer. With a
-      // conditional load the compiler would have to assume the load may be
-      // missing and wait for the newer tile as well, serialising latency.
-      Tile ta, tb;
-      int k = tw;
-      if (k < ntiles) {
-        load_tile(ta, k);
-        while (true) {
-          load_tile(tb, k + TW < ntiles ? k + TW : k);
-          compute_tile(ta, cs + k * kTile, ce);
-          k += TW;
-          if (k >= ntiles) break;
-          load_tile(ta, k + TW < ntiles ? k + TW : k);
-          compute_tile(tb, cs + k * kTile, ce);
-          k += TW;
-          if (k >= ntiles) break;
-        }
-      }
-    }
-  }
-
   // Consume the tile starting at token ts (tokens >= ce are masked). Value
   // e (0..7) of this lane's scores, probabilities and V operand belongs to
-  // token ts + 16 * (e / 4) + 4 * lg + e % 4.
-  __device__ __forceinline__ void compute_tile(Tile& t, int ts, int ce) {
+  // token ts + 8 * lg + e.
+  __device__ __forceinline__ void compute(Tile& t, int ts, int ce, int lg) {
     const bool tail = ts + kTile > ce;
     half8 kop[2][Gm::kQkMfma];
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
         if constexpr (FP8) {
-          const u32x4 w = t.k[r][jj >> 1];
+          const u32x4 w = t.k[m][jj >> 1];
           const u32x2 hlf = (jj & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
-          kop[r][jj] = e4m3x8_to_half8(hlf);
+          kop[m][jj] = e4m3x8_to_half8(hlf);
         } else {
-          kop[r][jj] = as_half8(t.k[r][jj]);
+          kop[m][jj] = as_half8(t.k[m][jj]);
         }
       }
-    // valid tokens among this lane's 4 of each block
-    const int nv0 = ce - (ts + 4 * lg);
-    const int nv1 = ce - (ts + 16 + 4 * lg);
+    // valid tokens among this lane's 8
+    const int nv = ce - (ts + 8 * lg);
     if (tail) {
       // zero the V entries of tokens past the end, in place (a masked
       // probability of 0 times a NaN left in an unused slot is still NaN)
+      auto keep8 = [](int n) {        // fp8: bytes of the first n tokens
+        return n <= 0 ? 0u : (n >= 4 ? 0xFFFFFFFFu : (1u << (8 * n)) - 1u);
+      };
+      auto keep16 = [](int n, int w) {   // fp16: halves of tokens 2w, 2w+1
+        return (n > 2 * w ? 0x0000FFFFu : 0u) | (n > 2 * w + 1 ? 0xFFFF0000u : 0u);
+      };
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int nv = r ? nv1 : nv0;
-#pragma unroll
-        for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-          if constexpr (FP8) {
-            const uint32_t keep = nv <= 0 ? 0u : (nv >= 4 ? 0xFFFFFFFFu
-                                                          : (1u << (8 * nv)) - 1u);
-            t.v[r][jd] &= keep;
-          } else {
-            const uint32_t lo0 = nv > 0 ? 0x0000FFFFu : 0u;
-            const uint32_t hi0 = nv > 1 ? 0xFFFF0000u : 0u;
-            const uint32_t lo1 = nv > 2 ? 0x0000FFFFu : 0u;
-            const uint32_t hi1 = nv > 3 ? 0xFFFF0000u : 0u;
-            t.v[r][jd].x &= (lo0 | hi0);
-            t.v[r][jd].y &= (lo1 | hi1);
-          }
+      for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
+        if constexpr (FP8) {
+          t.v[jd].x &= keep8(nv);
+          t.v[jd].y &= keep8(nv - 4);
+        } else {
+          t.v[jd].x &= keep16(nv, 0);
+          t.v[jd].y &= keep16(nv, 1);
+          t.v[jd].z &= keep16(nv, 2);
+          t.v[jd].w &= keep16(nv, 3);
         }
       }
     }
     half8 vop[Gm::kPvMfma];
 #pragma unroll
     for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-      if constexpr (FP8) {
-        vop[jd] = e4m3x8_to_half8(u32x2{t.v[0][jd], t.v[1][jd]});
-      } else {
-        const u32x4 w = {t.v[0][jd].x, t.v[0][jd].y, t.v[1][jd].x, t.v[1][jd].y};
-        vop[jd] = as_half8(w);
-      }
+      if constexpr (FP8) vop[jd] = e4m3x8_to_half8(t.v[jd]);
+      else vop[jd] = as_half8(t.v[jd]);
     }
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
@@ -272,7 +215,7 @@ struct Decoder {
       if (tail) {
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if ((e & 3) >= (e < 4 ? nv0 : nv1)) sv[e] = -INFINITY;
+          if (e >= nv) sv[e] = -INFINITY;
       }
       float mt = sv[0];
 #pragma unroll
@@ -306,229 +249,465 @@ struct Decoder {
     }
   }
 
-  // Merge the token-parallel waves (log-sum-exp) and write either the fp16
-  // output (slot < 0) or partial slot `slot` of (b, h). All waves call this.
-  __device__ __forceinline__ void flush(int b, int h, int slot) {
+  // Per-head totals: the running sum reduced over the four lane groups.
+  __device__ __forceinline__ void reduce_sums() {
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
       lrun[hb] += xor_lanes(lrun[hb], 16);
       lrun[hb] += xor_lanes(lrun[hb], 32);
     }
-    __syncthreads();   // LDS flush buffers are free (previous flush read)
-    if (lg == 0) {
-#pragma unroll
-      for (int hb = 0; hb < NH; ++hb) {
-        sm.m[tw][(hw * NH + hb) * 16 + mrow] = mrun[hb];
-        sm.l[tw][(hw * NH + hb) * 16 + mrow] = lrun[hb];
-      }
-    }
-    __syncthreads();
-    float wown[NH][4], ltot[NH][4], mtot[NH][4];
+  }
+
+  // Write this wave's result rows for (b, h) after reduce_sums(): the fp16
+  // output (slot < 0) or partial slot `slot` (normalised o, natural lse).
+  __device__ __forceinline__ void write_rows(const AttnArgs& a, int b, int h,
+                                             int hw, int slot, int mrow, int lg) {
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        // totals of head row 4*lg+i live in the lanes whose column is that head
+        const float Lh = read_lane(lrun[hb], 4 * lg + i);
+        const float Mh = read_lane(mrun[hb], 4 * lg + i);
         const int hh = (hw * NH + hb) * 16 + 4 * lg + i;
-        float M = -INFINITY;
+        if (hh >= a.G) continue;
+        const int hq = h * a.G + hh;
+        const float inv = Lh > 0.0f ? oscale / Lh : 0.0f;
+        if (slot >= 0) {
+          const long long row = ((long long)b * a.Hq + hq) * a.S + slot;
+          float* o = a.ws_o + row * D;
 #pragma unroll
-        for (int t = 0; t < TW; ++t) M = fmaxf(M, sm.m[t][hh]);
-        float Lsum = 0.0f;
-        if (M != -INFINITY) {
+          for (int jd = 0; jd < Gm::kPvMfma; ++jd) o[16 * jd + mrow] = acc[hb][jd][i] * inv;
+          if (mrow == 0)
+            a.ws_lse[row] = Lh > 0.0f ? (Mh + __builtin_amdgcn_logf(Lh)) * kLn2 : -INFINITY;
+        } else {
+          _Float16* o = a.out + ((long long)b * a.Hq + hq) * D;
 #pragma unroll
-          for (int t = 0; t < TW; ++t)
-            Lsum += sm.l[t][hh] * __builtin_amdgcn_exp2f(sm.m[t][hh] - M);
+          for (int jd = 0; jd < Gm::kPvMfma; ++jd)
+            o[16 * jd + mrow] = (_Float16)(acc[hb][jd][i] * inv);
         }
-        wown[hb][i] = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sm.m[tw][hh] - M);
-        ltot[hb][i] = Lsum;
-        mtot[hb][i] = M;
       }
-    if constexpr (TW > 1) {
-      if (tw > 0) {
-#pragma unroll
-        for (int hb = 0; hb < NH; ++hb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int hh = (hw * NH + hb) * 16 + 4 * lg + i;
-            if (hh < a.G) {
-#pragma unroll
-              for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-                sm.acc[tw - 1][hh][16 * jd + mrow] = acc[hb][jd][i] * wown[hb][i];
-            }
-          }
-      }
-      __syncthreads();
-    }
-    if (tw == 0) {
-#pragma unroll
-      for (int hb = 0; hb < NH; ++hb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int hh = (hw * NH + hb) * 16 + 4 * lg + i;
-          if (hh >= a.G) continue;
-          const int hq = h * a.G + hh;
-          const float Lsum = ltot[hb][i];
-          const float inv = Lsum > 0.0f ? oscale / Lsum : 0.0f;
-          float vals[Gm::kPvMfma];
-#pragma unroll
-          for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-            float v = acc[hb][jd][i] * wown[hb][i];
-#pragma unroll
-            for (int t = 1; t < TW; ++t) v += sm.acc[t - 1][hh][16 * jd + mrow];
-            vals[jd] = v * inv;
-          }
-          if (slot >= 0) {
-            const long long row = ((long long)b * a.Hq + hq) * a.S + slot;
-            float* o = a.ws_o + row * D;
-#pragma unroll
-            for (int jd = 0; jd < Gm::kPvMfma; ++jd) o[16 * jd + mrow] = vals[jd];
-            if (mrow == 0)
-              a.ws_lse[row] = Lsum > 0.0f
-                                  ? (mtot[hb][i] + __builtin_amdgcn_logf(Lsum)) * kLn2
-                                  : -INFINITY;
-          } else {
-            _Float16* o = a.out + ((long long)b * a.Hq + hq) * D;
-#pragma unroll
-            for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-              o[16 * jd + mrow] = (_Float16)vals[jd];
-          }
-        }
-    }
   }
 };
+
+// A value every lane holds equally, moved to a scalar register.
+__device__ __forceinline__ int uniform(int v) {
+  return __builtin_amdgcn_readfirstlane(v);
+}
 
 __device__ __forceinline__ int clamp_len(int L, int cap) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
 
-// Single pass (or one split): one workgroup per (sequence, kv head).
+__device__ __forceinline__ int clamp_page(int p, int P) {
+  return p < 0 ? 0 : (p >= P ? P - 1 : p);
+}
+
+// ---------------------------------------------------------------------------
+// Single pass (or one split): one workgroup per (sequence, kv head); its
+// waves are NWH head-parallel groups times TW token-parallel waves whose
+// results merge through LDS.
+template <int NH, int NWH, int TW, int D>
+struct SharedMem {
+  static constexpr int kHeads = NWH * NH * 16;
+  int pages[kMaxPages];
+  float m[TW][kHeads];
+  float l[TW][kHeads];
+  float acc[TW > 1 ? TW - 1 : 1][kHeads][D];
+};
+
 template <int D, int BS, bool FP8, int NH, int NWH, int TW>
 __global__ __launch_bounds__(64 * NWH * TW)
 __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_attn_kernel(AttnArgs a) {
-  using Dec = Decoder<D, BS, FP8, NH, NWH, TW>;
-  __shared__ typename Dec::Smem sm;
-  Dec dec(a, sm);
+  using Gm = Geo<D, BS, FP8>;
+  using Tile = TileRegs<D, BS, FP8>;
+  using Smem = SharedMem<NH, NWH, TW, D>;
+  __shared__ Smem sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);   // scalar: uniform control flow
+  const int hw = wave % NWH, tw = wave / NWH;
+  const int mrow = lane & 15, lg = lane >> 4;
   const int h = blockIdx.x % a.Hkv;
   const int b = blockIdx.x / a.Hkv;
-  const int L = clamp_len(a.context_lens[b], a.max_blocks * BS);
-  dec.begin(b, h);
-  dec.run(b, h, 0, L);
-  dec.flush(b, h, a.mode == 1 ? 0 : -1);
-  if (a.mode == 1 && threadIdx.x == 0) a.ws_count[(long long)b * a.Hkv + h] = 1;
-}
+  const int L = clamp_len(load_uniform(a.context_lens + b), a.max_blocks * BS);
 
-// Split pass, stream-K: workgroup w covers global tiles [w*tpw, (w+1)*tpw)
-// of the sequence-major, then kv-head-major, then token order, where each
-// (sequence, kv head) has ceil(L/32) tiles. tpw = max(ceil(T / grid),
-// ceil(n_max / (S - 1))) keeps every (sequence, kv head) within S partials.
-template <int D, int BS, bool FP8, int NH, int NWH, int TW>
-__global__ __launch_bounds__(64 * NWH * TW)
-__attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
-void decode_attn_streamk_kernel(AttnArgs a) {
-  using Dec = Decoder<D, BS, FP8, NH, NWH, TW>;
-  __shared__ typename Dec::Smem sm;
-  const int cap = a.max_blocks * BS;
-  const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
+  HeadState<D, BS, FP8, NH> st;
+  st.begin(a, b, h, hw, mrow, lg);
+  const uint8_t* kbase = a.k_pages + (long long)h * Gm::kPageBytes;
+  const uint8_t* vbase = a.v_pages + (long long)h * Gm::kPageBytes;
+  const long long page_stride = (long long)a.Hkv * Gm::kPageBytes;
+  const int* bt_row = a.block_table + (long long)b * a.max_blocks;
 
-  // 1. per-thread share of sequences: tile counts, their sum and maximum
-  const int per = (a.B + nthr - 1) / nthr;
-  const int b_lo = min(a.B, tid * per), b_hi = min(a.B, b_lo + per);
-  int my_sum = 0, my_max = 0;
-  for (int b = b_lo; b < b_hi; ++b) {
-    const int n = (clamp_len(a.context_lens[b], cap) + kTile - 1) / kTile;
-    my_sum += n;
-    my_max = max(my_max, n);
-  }
-  // block-wide inclusive scan of my_sum (Hillis-Steele in LDS) and max
-  sm.scan[tid] = my_sum;
-  __syncthreads();
-  for (int off = 1; off < nthr; off <<= 1) {
-    const int v = tid >= off ? sm.scan[tid - off] : 0;
+  for (int cs = 0; cs < L; cs += kMaxPages * BS) {
+    const int ce = min(L, cs + kMaxPages * BS);
+    const int p0 = cs / BS;
+    const int np = (ce - 1) / BS - p0 + 1;
+    __syncthreads();   // previous chunk's ids are free
+    for (int i = threadIdx.x; i < np; i += blockDim.x)
+      sm.pages[i] = clamp_page(bt_row[p0 + i], a.P);
     __syncthreads();
-    sm.scan[tid] += v;
-    __syncthreads();
-  }
-  const int seq_tiles = sm.scan[nthr - 1];
-  const int excl = sm.scan[tid] - my_sum;
-  __syncthreads();
-  sm.scan[tid] = my_max;
-  __syncthreads();
-  for (int off = nthr >> 1; off > 0; off >>= 1) {
-    if (tid < off) sm.scan[tid] = max(sm.scan[tid], sm.scan[tid + off]);
-    __syncthreads();
-  }
-  const int n_max = sm.scan[0];
-
-  const long long T = (long long)seq_tiles * a.Hkv;
-  long long tpw = (T + gridDim.x - 1) / gridDim.x;
-  const long long need = (n_max + (a.S - 1) - 1) / (a.S - 1);
-  if (tpw < need) tpw = need;
-  if (tpw < 1) tpw = 1;
-  const long long r0 = (long long)blockIdx.x * tpw;
-  if (r0 >= T) return;                        // whole workgroup leaves
-  const long long r1 = min(T, r0 + tpw);
-
-  // 2. locate the sequence holding global tile r0 (offsets scale by Hkv)
-  if (tid == 0) sm.loc[0] = -1;
-  __syncthreads();
-  {
-    long long off = (long long)excl * a.Hkv;
-    if (r0 >= off && r0 < off + (long long)my_sum * a.Hkv) {
-      for (int b = b_lo; b < b_hi; ++b) {
-        const int n = (clamp_len(a.context_lens[b], cap) + kTile - 1) / kTile;
-        const long long span = (long long)n * a.Hkv;
-        if (r0 < off + span) {
-          sm.loc[0] = b;
-          sm.loc[1] = (int)((r0 - off) / n);      // kv head
-          sm.loc[2] = (int)((r0 - off) % n);      // tile within (b, h)
-          break;
-        }
-        off += span;
+    const int ntiles = (ce - cs + kTile - 1) / kTile;
+    const int last_blk = (ce - 1) & ~15;
+    auto issue = [&](Tile& t, int k) {
+      const int ts = cs + k * kTile;
+      long long off[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int tb = min(ts + 16 * r, last_blk);
+        off[r] = sm.pages[tb / BS - p0] * page_stride + (tb % BS) * Gm::kRowBytes;
+      }
+      load_tile<D, BS, FP8>(t, kbase, vbase, off[0], off[1], lane);
+    };
+    // Two register tiles in flight; the next tile's loads are issued on
+    // every iteration, unconditionally (past the last tile they re-read the
+    // current one, already in L2), so the compiler waits only for the older
+    // tile's loads.
+    Tile ta, tb;
+    int k = tw;
+    if (k < ntiles) {
+      issue(ta, k);
+      while (true) {
+        issue(tb, k + TW < ntiles ? k + TW : k);
+        st.compute(ta, cs + k * kTile, ce, lg);
+        k += TW;
+        if (k >= ntiles) break;
+        issue(ta, k + TW < ntiles ? k + TW : k);
+        st.compute(tb, cs + k * kTile, ce, lg);
+        k += TW;
+        if (k >= ntiles) break;
       }
     }
   }
-  __syncthreads();
-  int b = sm.loc[0], h = sm.loc[1], tile = sm.loc[2];
-  long long base = r0 - tile;                 // global index of (b, h)'s tile 0
 
-  Dec dec(a, sm);
-  long long pos = r0;
-  while (pos < r1) {
-    const int L = clamp_len(a.context_lens[b], cap);
-    const int n = (L + kTile - 1) / kTile;
-    const int t_end = (int)min((long long)n, tile + (r1 - pos));
-    dec.begin(b, h);
-    dec.run(b, h, tile * kTile, min(t_end * kTile, L));
-    const int slot = (int)(blockIdx.x - base / tpw);
-    dec.flush(b, h, slot);
-    if (t_end == n && tid == 0) a.ws_count[(long long)b * a.Hkv + h] = slot + 1;
-    pos += t_end - tile;
-    base += n;
-    tile = 0;
-    if (++h == a.Hkv) {
-      h = 0;
-      do { ++b; } while (b < a.B && pos < r1 &&
-                         clamp_len(a.context_lens[b], cap) == 0);
+  // merge the token-parallel waves (log-sum-exp) through LDS
+  st.reduce_sums();
+  if constexpr (TW > 1) {
+    if (lg == 0) {
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb) {
+        sm.m[tw][(hw * NH + hb) * 16 + mrow] = st.mrun[hb];
+        sm.l[tw][(hw * NH + hb) * 16 + mrow] = st.lrun[hb];
+      }
     }
+    __syncthreads();
+    // rescale this wave's rows to the common max and totals
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
+      const int hcol = (hw * NH + hb) * 16 + mrow;      // column head of lane
+      float M = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < TW; ++t) M = fmaxf(M, sm.m[t][hcol]);
+      float Ls = 0.0f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+          Ls += sm.l[t][hcol] * __builtin_amdgcn_exp2f(sm.m[t][hcol] - M);
+      }
+      const float w = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st.mrun[hb] - M);
+      // rows 4*lg+i of acc scale by the weight of head 4*lg+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float wi = read_lane(w, 4 * lg + i);
+#pragma unroll
+        for (int jd = 0; jd < Gm::kPvMfma; ++jd) st.acc[hb][jd][i] *= wi;
+      }
+      st.mrun[hb] = M;
+      st.lrun[hb] = Ls;
+    }
+    if (tw > 0) {
+#pragma unroll
+      for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int hh = (hw * NH + hb) * 16 + 4 * lg + i;
+          if (hh < a.G) {
+#pragma unroll
+            for (int jd = 0; jd < Gm::kPvMfma; ++jd)
+              sm.acc[tw - 1][hh][16 * jd + mrow] = st.acc[hb][jd][i];
+          }
+        }
+    }
+    __syncthreads();
+    if (tw > 0) return;
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = (hw * NH + hb) * 16 + 4 * lg + i;
+        if (hh < a.G) {
+#pragma unroll
+          for (int jd = 0; jd < Gm::kPvMfma; ++jd)
+#pragma unroll
+            for (int t = 1; t < TW; ++t) st.acc[hb][jd][i] += sm.acc[t - 1][hh][16 * jd + mrow];
+        }
+      }
+  }
+  st.write_rows(a, b, h, hw, a.mode == 1 ? 0 : -1, mrow, lg);
+  if (a.mode == 1 && threadIdx.x == 0) a.ws_count[(long long)b * a.Hkv + h] = 1;
+}
+
+// ---------------------------------------------------------------------------
+// Split pass (stream-K).
+
+// Tiles of sequence b (its context clamped to the block table's capacity).
+__device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b, int cap) {
+  return (clamp_len(a.context_lens[b], cap) + kTile - 1) / kTile;
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_sum(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int u = __shfl_up(v, off, 64);
+    if (lane >= off) v += u;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Position in the split pass's tile order: (sequence b, kv head h, tile t
+// of n), L = tokens of b, base = global index of (b, h)'s first tile.
+struct Cursor {
+  int b, h, t, n, L;
+  long long base;
+};
+
+// The tile after c (one must exist): next tile, next kv head, or the next
+// sequence that has tokens.
+__device__ __forceinline__ Cursor advance(const AttnArgs& a, Cursor c, int cap) {
+  if (c.t + 1 < c.n) { ++c.t; return c; }
+  c.t = 0;
+  c.base += c.n;
+  if (++c.h < a.Hkv) return c;
+  c.h = 0;
+  do {
+    ++c.b;
+    c.L = clamp_len(load_uniform(a.context_lens + c.b), cap);
+  } while (c.L == 0);
+  c.n = (c.L + kTile - 1) / kTile;
+  return c;
+}
+
+// Byte offsets (head included) of the two 16-token blocks of c's tile. A
+// block wholly past the end re-reads the first one (in bounds; masked).
+template <int D, int BS, bool FP8>
+__device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
+                                             long long& off0, long long& off1) {
+  using Gm = Geo<D, BS, FP8>;
+  const int* bt_row = a.block_table + (long long)c.b * a.max_blocks;
+  const long long page_stride = (long long)a.Hkv * Gm::kPageBytes;
+  const long long head = (long long)c.h * Gm::kPageBytes;
+  const int ts = c.t * kTile;
+  const int pA = clamp_page(load_uniform(bt_row + ts / BS), a.P);
+  off0 = head + pA * page_stride + (ts % BS) * Gm::kRowBytes;
+  if (ts + 16 >= c.L) {
+    off1 = off0;
+  } else if constexpr (BS == 16) {
+    off1 = head + clamp_page(load_uniform(bt_row + ts / 16 + 1), a.P) * page_stride;
+  } else {
+    off1 = off0 + Gm::kBlockBytes;
+  }
+}
+
+// Merge the nparts partials of (b, h) from the workspace into out (fp16),
+// one wave.
+template <int D>
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
+                                               int nparts, int lane) {
+  for (int idx = lane; idx < a.G * D; idx += 64) {
+    const int g = idx / D, dim = idx % D;
+    const long long row = ((long long)b * a.Hq + h * a.G + g) * a.S;
+    float M = -INFINITY;
+    for (int i = 0; i < nparts; ++i) M = fmaxf(M, a.ws_lse[row + i]);
+    float num = 0.0f, den = 0.0f;
+    for (int i = 0; i < nparts; ++i) {
+      const float w = __builtin_amdgcn_exp2f((a.ws_lse[row + i] - M) * kLog2e);
+      den += w;
+      num += w * a.ws_o[(row + i) * D + dim];
+    }
+    a.out[((long long)b * a.Hq + h * a.G + g) * D + dim] =
+        (_Float16)(den > 0.0f ? num / den : 0.0f);
+  }
+}
+
+// Worker k (a wave, or NWH waves with head blocks split between them)
+// covers global tiles [k*tpw, (k+1)*tpw) of the sequence-major, then
+// kv-head-major, then token order, where each (sequence, kv head) has
+// ceil(L/32) tiles; tpw = max(ceil(T / workers), ceil(n_max / (S - 1)))
+// keeps every (sequence, kv head) within S partials. mode 2 writes the
+// partials and their count; mode 3 merges too: a (sequence, kv head) held
+// by one worker is written out directly, otherwise the last of its workers
+// to finish (an atomic counter per (sequence, kv head), returned to zero
+// afterwards) merges the partials.
+template <int D, int BS, bool FP8, int NH, int NWH>
+__global__ __launch_bounds__(256)
+__attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
+void decode_attn_stream_kernel(AttnArgs a) {
+  using Tile = TileRegs<D, BS, FP8>;
+  constexpr int kWorkersPerWg = 4 / NWH;
+  const int lane = threadIdx.x & 63;
+  // the wave index in a scalar register, so that the worker's share, the
+  // loop control and the block-table reads are scalar: a vector load of a
+  // page id would have to wait for the tile loads issued before it
+  const int wave = uniform(threadIdx.x >> 6);
+  const int hw = wave % NWH;
+  const int mrow = lane & 15, lg = lane >> 4;
+  const int workers = gridDim.x * kWorkersPerWg;
+  const int worker = blockIdx.x * kWorkersPerWg + wave / NWH;
+  const int cap = a.max_blocks * BS;
+
+  // 1. total tiles and the longest sequence (every wave, redundantly)
+  int carry = 0, n_max = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+    carry += __shfl(wave_incl_sum(n, lane), 63, 64);
+    n_max = max(n_max, wave_max(n));
+  }
+  carry = uniform(carry);
+  n_max = uniform(n_max);
+  const long long T = (long long)carry * a.Hkv;
+  long long tpw = (T + workers - 1) / workers;
+  const long long need = (n_max + (a.S - 1) - 1) / (a.S - 1);
+  if (tpw < need) tpw = need;
+  if (tpw < 1) tpw = 1;
+
+  if (a.mode == 3 && hw == 0) {
+    // sequences without tokens get zeros (no worker covers them)
+    for (int b = worker; b < a.B; b += workers) {
+      if (clamp_len(a.context_lens[b], cap) != 0) continue;
+      for (int i = lane; i < a.Hq * D; i += 64)
+        a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
+    }
+  }
+  const long long r0 = (long long)worker * tpw;
+  if (r0 >= T) return;                        // this wave has no share
+  const long long r1 = min(T, r0 + tpw);
+
+  // 2. the sequence, kv head and tile of global tile r0
+  Cursor c{0, 0, 0, 1, 1, 0};
+  {
+    long long done = 0;                       // tiles (times Hkv) before chunk
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+      const int incl = wave_incl_sum(n, lane);
+      const long long lo = done + (long long)(incl - n) * a.Hkv;
+      const long long hi = done + (long long)incl * a.Hkv;
+      const unsigned long long hit = __ballot(r0 >= lo && r0 < hi);
+      if (hit) {
+        const int src = __ffsll((long long)hit) - 1;
+        c.b = c0 + src;
+        c.n = __shfl(n, src, 64);
+        const long long rel = r0 - __shfl(lo, src, 64);
+        c.h = (int)(rel / c.n);
+        c.t = (int)(rel % c.n);
+        break;
+      }
+      done += (long long)__shfl(incl, 63, 64) * a.Hkv;
+    }
+  }
+  c.b = uniform(c.b);
+  c.h = uniform(c.h);
+  c.t = uniform(c.t);
+  c.n = uniform(c.n);
+  c.L = clamp_len(load_uniform(a.context_lens + c.b), cap);
+  c.base = r0 - c.t;
+
+  HeadState<D, BS, FP8, NH> st;
+  st.begin(a, c.b, c.h, hw, mrow, lg);
+
+  // End of (b, h)'s segment in this share: partial or output, and merge.
+  auto finish = [&](const Cursor& s) {
+    st.reduce_sums();
+    const long long first = s.base / tpw, last = (s.base + s.n - 1) / tpw;
+    const int slot = (int)(worker - first);
+    if (a.mode == 3 && first == last) {
+      st.write_rows(a, s.b, s.h, hw, -1, mrow, lg);
+      return;
+    }
+    st.write_rows(a, s.b, s.h, hw, slot, mrow, lg);
+    if (a.mode == 2) {
+      if (s.t == s.n - 1 && hw == 0 && lane == 0)
+        a.ws_count[(long long)s.b * a.Hkv + s.h] = slot + 1;
+      return;
+    }
+    // Publish the partial and count arrivals (NWH per worker); the last
+    // to arrive merges. The device-scope acquire-release atomic waits for
+    // this wave's partial stores and writes them back for the other XCDs,
+    // and for the merger drops stale cache lines before it reads.
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 1,
+                                   __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, 64);
+    const int arrivals = (int)(last - first + 1) * NWH;
+    if (old == arrivals - 1) {
+      merge_partials<D>(a, s.b, s.h, (int)(last - first + 1), lane);
+      if (lane == 0)
+        __hip_atomic_store(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 0,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  const uint8_t* kp = a.k_pages;
+  const uint8_t* vp = a.v_pages;
+  Tile ta, tb;
+  long long o0, o1;
+  tile_offsets<D, BS, FP8>(a, c, o0, o1);
+  load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane);
+  long long pos = r0;
+  // One pipeline over the whole share: the next tile's loads (even in the
+  // next segment) are in flight while the current tile is computed. They
+  // are issued unconditionally (past the share's end they re-read the
+  // current tile) so that the compiler waits only for the older tile.
+  while (true) {
+    bool more = pos + 1 < r1;
+    Cursor nx = more ? advance(a, c, cap) : c;
+    tile_offsets<D, BS, FP8>(a, nx, o0, o1);
+    load_tile<D, BS, FP8>(tb, kp, vp, o0, o1, lane);
+    st.compute(ta, c.t * kTile, c.L, lg);
+    if (!more || nx.b != c.b || nx.h != c.h) {
+      finish(c);
+      if (!more) break;
+      st.begin(a, nx.b, nx.h, hw, mrow, lg);
+    }
+    ++pos;
+    c = nx;
+
+    more = pos + 1 < r1;
+    nx = more ? advance(a, c, cap) : c;
+    tile_offsets<D, BS, FP8>(a, nx, o0, o1);
+    load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane);
+    st.compute(tb, c.t * kTile, c.L, lg);
+    if (!more || nx.b != c.b || nx.h != c.h) {
+      finish(c);
+      if (!more) break;
+      st.begin(a, nx.b, nx.h, hw, mrow, lg);
+    }
+    ++pos;
+    c = nx;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Instances: head_dim {64, 128} x block_size {16, 32, 64} x {fp16, fp8} x
-// group-size class (heads per workgroup = NWH * NH * 16).
+// group-size class.
 template <int D, int BS, bool FP8, int NH, int NWH, int TW>
 static hipError_t launch_cfg(const AttnArgs& a, hipStream_t st) {
-  constexpr int kThreads = 64 * NWH * TW;
-  if (a.mode == 2) {
+  if (a.mode >= 2) {
     // persistent grid: as many workgroups as fit at once on 256 CUs
     constexpr int kPerCu = NH == 1 ? 2 : 1;
-    hipLaunchKernelGGL((decode_attn_streamk_kernel<D, BS, FP8, NH, NWH, TW>),
-                       256u * kPerCu, kThreads, 0, st, a);
+    hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH>),
+                       256u * kPerCu, 256, 0, st, a);
   } else {
     const unsigned grid = (unsigned)((long long)a.B * a.Hkv);
     hipLaunchKernelGGL((decode_attn_kernel<D, BS, FP8, NH, NWH, TW>), grid,
-                       kThreads, 0, st, a);
+                       64 * NWH * TW, 0, st, a);
   }
   return hipGetLastError();
 }
@@ -539,7 +718,7 @@ static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
   if (a.G <= 32) return launch_cfg<D, BS, FP8, 2, 1, 4>(a, st);
   if (a.G <= 64) return launch_cfg<D, BS, FP8, 2, 2, 2>(a, st);
   if (a.G <= 96) return launch_cfg<D, BS, FP8, 3, 2, 2>(a, st);
-  if (a.G <= 128) return launch_cfg<D, BS, FP8, 4, 2, 1>(a, st);
+  if (a.G <= 128) return launch_cfg<D, BS, FP8, 4, 2, 2>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -86,6 +86,17 @@ __device__ __forceinline__ float xor_lanes(float v, int mask) {
       __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(v)));
 }
 
+// Load of a value that every lane addresses alike (block-table entry,
+// context length, scale) through the constant address space, so that it
+// becomes a scalar load: it then waits on the scalar counter and never
+// holds back the vector loads of K/V tiles. The memory must not change
+// while the kernel runs (true for these inputs).
+template <typename T>
+__device__ __forceinline__ T load_uniform(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(
+      __builtin_bit_cast(unsigned long long, p));
+}
+
 __device__ __forceinline__ float read_lane(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }

@@ -8,7 +8,7 @@
 // One thread handles two adjacent dimensions of one (token, kv head) row:
 // it reads 4 bytes of k_new and of v_new and writes them (or their two fp8
 // codes) at the positions the page layout gives them: both K values sit in
-// one 16-byte chunk; the two V values are 4 elements apart.
+// one 16-byte chunk; the two V values are 8 elements apart.
 #include "launch.h"
 #include "device_common.h"
 
@@ -37,15 +37,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
   // element offsets inside the (page, head) tile (16-token blocks)
   constexpr int X = FP8 ? 16 : 8;                     // elements per 16 B
   const int blk = slot >> 4, r = slot & 15;
+  // K rows of a block: slots 4..7 and 8..11 trade places (bits 2, 3 swapped)
+  const int krow = (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
   const long long tile = ((long long)page * a.Hkv + h) * a.bs * D;
-  const long long koff = tile + ((blk * (D / X) + dp / X) * 16 + r) * X + dp % X;
-  const long long voff = tile + (((blk * (D / 16) + dp / 16) * 4 + (r >> 2)) * 16 +
-                                 dp % 16) * 4 + (r & 3);
+  const long long koff = tile + ((blk * (D / X) + dp / X) * 16 + krow) * X + dp % X;
+  const long long voff = tile + (((blk * (D / 16) + dp / 16) * 2 + (r >> 3)) * 16 +
+                                 dp % 16) * 8 + (r & 7);
   if constexpr (!FP8) {
     *reinterpret_cast<uint32_t*>(a.k_pages + koff * 2) = kin;
     uint16_t* vdst = reinterpret_cast<uint16_t*>(a.v_pages) + voff;
     vdst[0] = (uint16_t)(vin & 0xFFFFu);
-    vdst[4] = (uint16_t)(vin >> 16);
+    vdst[8] = (uint16_t)(vin >> 16);
   } else {
     const float ks = a.k_scale[h];
     const float vs = a.v_scale[h];
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
     const uint32_t v1 = f32_to_e4m3fn(h2f(vin >> 16) / vs);
     *reinterpret_cast<uint16_t*>(a.k_pages + koff) = (uint16_t)(k0 | (k1 << 8));
     a.v_pages[voff] = (uint8_t)v0;
-    a.v_pages[voff + 4] = (uint8_t)v1;
+    a.v_pages[voff + 8] = (uint8_t)v1;
   }
 }
 

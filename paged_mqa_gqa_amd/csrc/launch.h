@@ -31,10 +31,12 @@ struct AttnArgs {
   float* ws_o;               // split pass: [B, Hq, S, D]
   float* ws_lse;             // split pass: [B, Hq, S]
   int32_t* ws_count;         // split pass: [B, Hkv] partials per (b, h)
+  int32_t* ws_sem;           // merged split pass: [B, Hkv] arrival counters
   float scale_log2;          // scale * log2(e)
   int B, Hq, Hkv, G, P, max_blocks, S;
   int mode;                  // 0: single pass -> out; 1: one split per
-                             // (b, h) -> slot 0; 2: stream-K split pass
+                             // (b, h) -> slot 0; 2: stream-K split pass;
+                             // 3: stream-K split pass merged in-kernel
 };
 
 struct ReduceArgs {

@@ -31,7 +31,7 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
-              "paged_decode_attn_splitk_reduce",
+              "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
               "paged_decode_attn_splitk_workspace_size",
               "paged_decode_attn_suggest_splits", "pa_status_string", "pa_version"]:
         assert n in names
@@ -97,7 +97,7 @@ def test_splitk_validation():
     lib = pa.load()
     d = good_dims()
     need = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 4)
-    assert need == 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4 + 2 * 2 * 4
+    assert need == 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4 + 2 * 2 * 2 * 4
     assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 0) == 0
     call = lambda S, ws, n: lib.paged_decode_attn_splitk(
         ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, S, ws, n, None)
@@ -111,6 +111,12 @@ def test_splitk_validation():
     assert red(0, FAKE, need) == -4
     assert red(4, FAKE, need, None) == -1
     assert red(4, FAKE, need, FAKE, None) == -1
+    mer = lambda S, ws, n, out=FAKE: lib.paged_decode_attn_splitk_merged(
+        ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, S, ws, n, out, None)
+    assert mer(0, FAKE, need) == -4
+    assert mer(4, FAKE, need - 1) == -5
+    assert mer(4, None, need) == -5
+    assert mer(4, FAKE, need, None) == -1
 
 
 def test_kv_append_validation():

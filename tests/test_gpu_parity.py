@@ -43,9 +43,15 @@ def pa_mod():
     return pa
 
 
-def gpu_decode(dw, num_splits=1):
+def gpu_decode(dw, num_splits=1, merged=False):
     pa = pa_mod()
-    if num_splits == 1:
+    if merged:
+        ws = pa.splitk_workspace(dw.q, dw.k_pages, dw.block_table, num_splits)
+        out = pa.paged_decode_attn_splitk_merged(dw.q, dw.k_pages, dw.v_pages,
+                                                 dw.block_table, dw.context_lens,
+                                                 dw.scale, num_splits, ws,
+                                                 dw.k_scale, dw.v_scale)
+    elif num_splits == 1:
         out = pa.paged_decode_attn(dw.q, dw.k_pages, dw.v_pages, dw.block_table,
                                    dw.context_lens, dw.scale, dw.k_scale, dw.v_scale)
     else:
@@ -192,6 +198,44 @@ def test_decode_parity_sweep(case, kv_dtype):
 
 
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_merged_split_parity_sweep(case, kv_dtype):
+    """Split pass with the in-kernel merge, same sweep and bounds."""
+    Hq, Hkv, d, bs, lens = SWEEP[case]
+    say("merged", kv_dtype, SWEEP[case])
+    w = make_case(len(lens), Hq, Hkv, d, bs, lens, kv_dtype=kv_dtype,
+                  seed=100 + case, extra_pages=2)
+    dw = DeviceWorkload(w)
+    ref = oracle_out(w)
+    for S in (2, 5, 64):
+        err = max_err(gpu_decode(dw, S, merged=True), ref)
+        assert err <= TOL[kv_dtype], (S, err)
+
+
+def test_merged_counters_return_to_zero_across_calls():
+    """Three merged calls in a row on one workspace, the middle one on a
+    different (smaller) batch: every result matches, counters end at zero."""
+    say("merged reuse")
+    pa = pa_mod()
+    w1 = make_case(4, 32, 8, 128, 16, (3000, 0, 700, 64), seed=303)
+    w2 = make_case(4, 32, 8, 128, 16, (100, 50, 0, 1), seed=304)
+    d1, d2 = DeviceWorkload(w1), DeviceWorkload(w2)
+    S = 16
+    ws = pa.splitk_workspace(d1.q, d1.k_pages, d1.block_table, S)
+    ref1, ref2 = oracle_out(w1), oracle_out(w2)
+    for dw, ref in ((d1, ref1), (d2, ref2), (d1, ref1)):
+        out = pa.paged_decode_attn_splitk_merged(dw.q, dw.k_pages, dw.v_pages,
+                                                 dw.block_table, dw.context_lens,
+                                                 dw.scale, S, ws)
+        assert max_err(out, ref) <= TOL["fp16"]
+        torch.cuda.synchronize()
+        _, _, _ = pa.split_views(ws, 4, 32, 8, S, 128)
+        n = 4 * 32 * S
+        sem = ws[(n * 128 + n) * 4 + 4 * 8 * 4:(n * 128 + n) * 4 + 2 * 4 * 8 * 4].view(torch.int32)
+        assert int(sem.abs().sum()) == 0
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
 @pytest.mark.parametrize("S", [1, 2, 3, 7, 16, 64])
 def test_split_pass_partials_and_merge(S, kv_dtype):
     """The split pass's ranges partition each context: their lse values
@@ -324,7 +368,9 @@ def test_full_size_workload(name):
     dw = DeviceWorkload(w, upto_last=True)
     pa.kv_append(dw.new_k, dw.new_v, dw.k_pages, dw.v_pages, dw.block_table,
                  dw.positions, k_scale=dw.k_scale, v_scale=dw.v_scale)
-    out = gpu_decode(dw, cfg.num_splits)
+    out = gpu_decode(dw, cfg.num_splits, merged=True)
+    out2 = gpu_decode(dw, cfg.num_splits)
+    assert torch.isfinite(out2.float()).all()
     seqs = FULL[name]
     if seqs is None and name == "mixed_fp8":
         rng = np.random.default_rng(0)
@@ -333,7 +379,9 @@ def test_full_size_workload(name):
         seqs = tuple(sorted(set([longest, shortest] + rng.choice(cfg.num_seqs, 6, replace=False).tolist())))
     ref = oracle_out(w, seqs)
     err = max_err(out, ref, seqs)
-    say("full", name, "max err", err)
+    err2 = max_err(out2, ref, seqs)
+    say("full", name, "max err merged", err, "two-pass", err2)
     assert err <= TOL[cfg.kv_dtype], err
+    assert err2 <= TOL[cfg.kv_dtype], err2
     # every other row must at least be finite
     assert torch.isfinite(out.float()).all()

@@ -14,19 +14,24 @@ from tests.oracle_cases import contiguous_reference_sdpa, oracle_decode, oracle_
 from workloads import make, make_case
 
 
+# storage row of each slot of a 16-token K block, written out by hand: the
+# second and third quads of slots trade places
+_K_ROW = [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+
+
 def _tile_pos_k(t, i, d, X=8):
     """Header layout, K: 16-token blocks, 16-byte chunks of X elements."""
     blk, r = divmod(t, 16)
     c, x = divmod(i, X)
-    return ((blk * (d // X) + c) * 16 + r) * X + x
+    return ((blk * (d // X) + c) * 16 + _K_ROW[r]) * X + x
 
 
 def _tile_pos_v(t, i, d):
-    """Header layout, V: 16-token blocks, 16-dim groups, token quads."""
+    """Header layout, V: 16-token blocks, 16-dim groups, token octets."""
     blk, r = divmod(t, 16)
     jd, n = divmod(i, 16)
-    q4, e = divmod(r, 4)
-    return (((blk * (d // 16) + jd) * 4 + q4) * 16 + n) * 4 + e
+    o, e = divmod(r, 8)
+    return (((blk * (d // 16) + jd) * 2 + o) * 16 + n) * 8 + e
 
 
 def _scatter_by_hand(K, V, perm_pages, bs, num_pages):

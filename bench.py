@@ -2,18 +2,22 @@
 """Benchmark one decode step of paged MQA/GQA attention on one MI355X.
 
 A step is the whole hot path over one batch: kv_append of every sequence's
-new token into its page, then decode attention (split pass plus
-log-sum-exp merge, or the single pass when the workload uses one split).
-Inputs are seeded synthetic data already resident in HBM; R replicas of the
-KV pools rotate step to step so that the 256 MB Infinity Cache cannot serve
-the working set.
+new token into its page, then decode attention over the sequence's context
+(the split pass with its log-sum-exp merge, in one call, or the single pass
+when the workload uses one split). Inputs are seeded synthetic data already
+resident in HBM. R replicas of the KV pools rotate step to step so that the
+256 MB Infinity Cache cannot serve the working set. Each replica's step is
+captured once as a HIP graph and replayed, so the timed steps are the GPU's
+own time and not Python's launch overhead.
 
 Prints ONE JSON line: metric / value (KV GB/s of the step) / unit, timing,
 `roofline` for the attention kernel (algorithmic bytes per launch / its
-average event-timed duration, against 8 TB/s) and `cpu_baseline` (the fp64
-oracle timed on this host over a bounded sample of the same workload).
+average event-timed launch duration, against 8 TB/s) and `cpu_baseline`
+(the fp64 oracle timed on this host over a bounded sample of the same
+workload).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --copy-only BYTES     # plain copy kernel for counter scaling
 """
 from __future__ import annotations
 
@@ -31,7 +35,9 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "gqa_llama"
 METRIC = "decode-attn KV GB/s (% of HBM peak) + us/call, GQA 32q/8kv d128 batch 32"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SRC = os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", "decode_attn.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
+                  for f in ("decode_attn.hip", "device_common.h", "launch.h")]
+ATTN_LAUNCHES_PER_GRAPH = 8
 
 
 def parse():
@@ -44,17 +50,22 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="override pool replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES, --steps times")
     return ap.parse_args()
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources; else None."""
     path = os.path.join(PROFILE_DIR, f"decode_attn_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
@@ -73,20 +84,20 @@ def measured_traffic(workload: str):
 
 def attention_algorithmic_bytes(w) -> int:
     """Bytes decode attention must move at minimum: K/V of every attended
-    token, q, the block-table entries of those tokens, the context lengths
-    and the fp16 output (split partials are this implementation's overhead,
-    not counted)."""
+    token, q, the fp16 output, the block-table entries of those tokens, the
+    context lengths and (fp8) the scales. Split partials are this
+    implementation's overhead and are not counted."""
     cfg = w.cfg
     L = w.context_lens.astype("int64")
     nblk = -(-L // cfg.block_size)
     qb = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 2
+    scales = 0 if cfg.kv_dtype == "fp16" else 2 * cfg.num_kv_heads * 4
     return int(w.kv_bytes() + 2 * qb + int(nblk.sum()) * 4 * cfg.num_kv_heads
-               + cfg.num_seqs * 4)
+               + cfg.num_seqs * 4 + scales)
 
 
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the same step."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -126,12 +137,30 @@ def cpu_baseline(w, budget_s: float):
     }
 
 
+def copy_only(nbytes: int, steps: int):
+    """A plain streaming kernel of known size (reads nbytes, writes nbytes):
+    the reference for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = nbytes // 2
+    src = torch.randn(n, device="cuda", dtype=torch.float32).to(torch.float16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 2, "copy_bytes_written": n * 2,
+                      "launches": steps}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported "
               f"(this library has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_only:
+        copy_only(args.copy_only, args.steps)
+        return
     import numpy as np
     import torch
     import paged_mqa_gqa_amd as pa
@@ -152,49 +181,70 @@ def main():
     pools = [(dw.k_pages, dw.v_pages)] + [(dw.k_pages.clone(), dw.v_pages.clone())
                                           for _ in range(R - 1)]
     stream = torch.cuda.Stream()     # the stream every kernel goes to
-    d = pa.dims(cfg.num_seqs, cfg.num_q_heads, dw.k_pages, dw.block_table)
     ws = pa.splitk_workspace(dw.q, dw.k_pages, dw.block_table, S)
     out = torch.empty_like(dw.q)
-    torch.cuda.synchronize()
+    group = cfg.num_q_heads // cfg.num_kv_heads
 
-    def step(i, ev=None):
-        kp, vp = pools[i % R]
+    def append(r):
+        kp, vp = pools[r]
         pa.kv_append(dw.new_k, dw.new_v, kp, vp, dw.block_table, dw.positions,
                      k_scale=dw.k_scale, v_scale=dw.v_scale, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+
+    def attention(r):
+        kp, vp = pools[r]
         if S == 1:
             pa.paged_decode_attn(dw.q, kp, vp, dw.block_table, dw.context_lens,
                                  dw.scale, dw.k_scale, dw.v_scale, out=out, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
         else:
             pa.paged_decode_attn_splitk_merged(dw.q, kp, vp, dw.block_table,
                                                dw.context_lens, dw.scale, S, ws,
                                                dw.k_scale, dw.v_scale, out=out,
                                                stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        return g
+
+    # eager run of every call once (first-use work stays out of the graphs)
+    with torch.cuda.stream(stream):
+        for r in range(R):
+            append(r)
+            attention(r)
+    torch.cuda.synchronize()
+    step_graphs = [capture(lambda r=r: (append(r), attention(r))) for r in range(R)]
+    attn_graph = capture(lambda: [attention(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
+    torch.cuda.synchronize()
 
     with torch.cuda.stream(stream):
         for i in range(args.warmup):
-            step(i)
+            step_graphs[i % R].replay()
     torch.cuda.synchronize()
 
     # timed region: exactly K steps, synchronised on both sides
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
     with torch.cuda.stream(stream):
         for i in range(args.steps):
-            step(i, events[i])
+            step_graphs[i % R].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
     ms_step = elapsed * 1e3 / args.steps
-    attn_us = [a.elapsed_time(b) * 1e3 for a, b in events]
-    attn_avg_us = float(np.mean(attn_us))
+
+    # attention launch duration: HIP events on the launch stream around
+    # replays of back-to-back attention launches (same rotation of pools)
+    reps = max(4, args.steps // ATTN_LAUNCHES_PER_GRAPH)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        attn_graph.replay()
+        e0.record(stream)
+        for _ in range(reps):
+            attn_graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    attn_avg_us = e0.elapsed_time(e1) * 1e3 / (reps * ATTN_LAUNCHES_PER_GRAPH)
+
     value = kvb / (ms_step * 1e-3) / 1e9
     alg = attention_algorithmic_bytes(w)
     achieved = alg / (attn_avg_us * 1e-6) / 1e9
@@ -204,6 +254,13 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
 
+    if S == 1:
+        attn_desc, kernel = "single pass", "decode_attn_kernel"
+    elif group <= 16:
+        attn_desc, kernel = "split pass with in-kernel merge", "decode_attn_stream_kernel"
+    else:
+        attn_desc = "split pass + reduce kernel"
+        kernel = "decode_attn_stream_kernel (+ splitk_reduce_kernel)"
     res = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -216,14 +273,14 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp16" if cfg.kv_dtype == "fp16" else "fp8_e4m3fn",
-        "data": "synthetic",
+        "data": "synthetic (seeded; no dataset or weights involved)",
         "config": {
             "workload": cfg.name, "batch": cfg.num_seqs, "q_heads": cfg.num_q_heads,
             "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
-            "context_tokens": int(w.context_lens.sum()), "splits": S,
-            "pool_replicas": R, "step": "kv_append + attention" +
-            (" (single pass)" if S == 1 else " (split pass with in-kernel merge)"),
+            "context_tokens": int(w.context_lens.sum()), "kv_bytes": int(kvb),
+            "splits": S, "pool_replicas": R,
+            "step": f"kv_append + attention ({attn_desc}), one HIP graph per replica",
         },
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "us_per_step": round(ms_step * 1e3, 2),
@@ -234,9 +291,9 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": ("decode_attn_kernel (single pass)" if S == 1 else
-                       "decode_attn_streamk_kernel (split pass, merged)"),
+            "kernel": kernel,
             "algorithmic_bytes_per_launch": alg,
+            "launch_us": round(attn_avg_us, 3),
         },
         "cpu_baseline": cpu,
     }

@@ -211,19 +211,22 @@ int paged_decode_attn_splitk_reduce(const pa_dims* dims,
                                     hipStream_t stream);
 
 /*
- * paged_decode_attn_splitk_merged — split decode attention in one launch.
+ * paged_decode_attn_splitk_merged — split decode attention in one call.
  *
  * Same split as paged_decode_attn_splitk (ranges of the batch's tiles over
  * a persistent grid, at most num_splits per (sequence, kv head)), with the
- * log-sum-exp merge done in the same kernel: a (sequence, kv head) covered
- * by one workgroup is normalised and written straight to `out`; otherwise
- * each of its workgroups writes its partial to the workspace and counts its
- * arrival on sem[b, h] (device-scope atomic after a device-scope fence),
- * and the last to arrive merges the partials into `out` and resets
- * sem[b, h] to zero. out [B, Hq, d] fp16 is the same result as
- * paged_decode_attn up to rounding; sequences with L = 0 get zeros.
- * Two merged calls that share one workspace must not run concurrently.
- * num_splits == 1 runs paged_decode_attn (workspace unused).
+ * log-sum-exp merge done in the same kernel when the group has at most 16
+ * q heads: a (sequence, kv head) covered by one worker is normalised and
+ * written straight to `out`; otherwise each of its workers writes its
+ * partial to the workspace with device-scope (write-through) stores, waits
+ * for them to complete, and counts its arrival on sem[b, h] with a
+ * device-scope atomic; the last to arrive reads the partials with
+ * device-scope loads, merges them into `out` and resets sem[b, h] to zero.
+ * Larger groups run paged_decode_attn_splitk and then
+ * paged_decode_attn_splitk_reduce on the same stream. out [B, Hq, d] fp16
+ * is the same result as paged_decode_attn up to rounding; sequences with
+ * L = 0 get zeros. Two merged calls that share one workspace must not run
+ * concurrently. num_splits == 1 runs paged_decode_attn (workspace unused).
  */
 int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
                                     const void* k_pages, const void* v_pages,

@@ -186,6 +186,10 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
 }
 
+// Largest group size (q heads per kv head) whose partials the merged call
+// merges inside the attention kernel.
+constexpr int kMergeInKernelMaxGroup = 16;
+
 int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
                                     const void* k_pages, const void* v_pages,
                                     const int32_t* block_table,
@@ -209,6 +213,16 @@ int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
                              context_lens, scale, k_scale, v_scale, out, stream);
   if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
     return PA_ERR_WORKSPACE;
+  if (dims->num_q_heads / dims->num_kv_heads > kMergeInKernelMaxGroup) {
+    // wide groups: one wave cannot merge G heads quickly; the reduce kernel
+    // spreads the merge over a wave per (sequence, q head)
+    rc = paged_decode_attn_splitk(dims, q, k_pages, v_pages, block_table,
+                                  context_lens, scale, k_scale, v_scale,
+                                  num_splits, workspace, workspace_bytes, stream);
+    if (rc) return rc;
+    return paged_decode_attn_splitk_reduce(dims, context_lens, num_splits,
+                                           workspace, workspace_bytes, out, stream);
+  }
   pa::AttnArgs a = make_args(dims, q, k_pages, v_pages, block_table,
                              context_lens, scale, k_scale, v_scale);
   const WsViews v = ws_views(dims, num_splits, workspace);

@@ -82,7 +82,9 @@ struct TileRegs {
 };
 
 // Issue the loads of one tile whose two 16-token blocks start at byte
-// offsets off0 / off1 of the K and V pools (head offset included).
+// offsets off0 / off1 of the K and V pools (head offset included). K/V are
+// read once per call, so the loads are nontemporal (streamed past the
+// caches' retention).
 //
 // Token order inside the tile: QK MFMA m (0, 1) takes as its 16 A rows the
 // tokens 8 * (R / 4) + 4 * m + R % 4 (R = 0..15), i.e. rows 0..7 from block
@@ -103,12 +105,13 @@ __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int jl = 0; jl < Gm::kKLoads; ++jl)
-      t.k[m][jl] = *reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl);
+      t.k[m][jl] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl));
   const uint8_t* vb = vbase + (lg < 2 ? off0 : off1) + ((lg & 1) * 16 + R) * 8 * Gm::kEsz;
 #pragma unroll
   for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-    t.v[jd] = *reinterpret_cast<const typename TileRegs<D, BS, FP8>::VT*>(
-        vb + jd * 256 * Gm::kEsz);
+    t.v[jd] = __builtin_nontemporal_load(
+        reinterpret_cast<const typename TileRegs<D, BS, FP8>::VT*>(vb + jd * 256 * Gm::kEsz));
 }
 
 // Attention state of one wave for NH blocks of 16 q heads of one (sequence,
@@ -260,6 +263,10 @@ struct HeadState {
 
   // Write this wave's result rows for (b, h) after reduce_sums(): the fp16
   // output (slot < 0) or partial slot `slot` (normalised o, natural lse).
+  // COHERENT partials are stored as device-scope atomics, i.e. written
+  // through to the level every compute unit reads, for a merge inside the
+  // same launch.
+  template <bool COHERENT = false>
   __device__ __forceinline__ void write_rows(const AttnArgs& a, int b, int h,
                                              int hw, int slot, int mrow, int lg) {
 #pragma unroll
@@ -276,10 +283,16 @@ struct HeadState {
         if (slot >= 0) {
           const long long row = ((long long)b * a.Hq + hq) * a.S + slot;
           float* o = a.ws_o + row * D;
+          const float lse = Lh > 0.0f ? (Mh + __builtin_amdgcn_logf(Lh)) * kLn2 : -INFINITY;
 #pragma unroll
-          for (int jd = 0; jd < Gm::kPvMfma; ++jd) o[16 * jd + mrow] = acc[hb][jd][i] * inv;
-          if (mrow == 0)
-            a.ws_lse[row] = Lh > 0.0f ? (Mh + __builtin_amdgcn_logf(Lh)) * kLn2 : -INFINITY;
+          for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
+            if constexpr (COHERENT) store_coherent(o + 16 * jd + mrow, acc[hb][jd][i] * inv);
+            else o[16 * jd + mrow] = acc[hb][jd][i] * inv;
+          }
+          if (mrow == 0) {
+            if constexpr (COHERENT) store_coherent(a.ws_lse + row, lse);
+            else a.ws_lse[row] = lse;
+          }
         } else {
           _Float16* o = a.out + ((long long)b * a.Hq + hq) * D;
 #pragma unroll
@@ -516,23 +529,76 @@ __device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
 }
 
 // Merge the nparts partials of (b, h) from the workspace into out (fp16),
-// one wave.
+// one wave: each lane owns 4 output values of one head for up to two heads
+// at a time and folds the partials in by an online log-sum-exp, the loads of
+// eight partials for both in flight together. The loads are device-scope
+// atomics, so they see the partials that other compute units wrote through
+// (write_rows<true>).
 template <int D>
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
                                                int nparts, int lane) {
-  for (int idx = lane; idx < a.G * D; idx += 64) {
-    const int g = idx / D, dim = idx % D;
-    const long long row = ((long long)b * a.Hq + h * a.G + g) * a.S;
-    float M = -INFINITY;
-    for (int i = 0; i < nparts; ++i) M = fmaxf(M, a.ws_lse[row + i]);
-    float num = 0.0f, den = 0.0f;
-    for (int i = 0; i < nparts; ++i) {
-      const float w = __builtin_amdgcn_exp2f((a.ws_lse[row + i] - M) * kLog2e);
-      den += w;
-      num += w * a.ws_o[(row + i) * D + dim];
+  constexpr int kCols = D / 4;
+  constexpr int kParts = 8;
+  const int items = a.G * kCols;
+  for (int base = 0; base < items; base += 128) {
+    long long row[2];
+    int c4[2];
+    bool live[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int it = base + 64 * u + lane;
+      live[u] = it < items;
+      const int itc = live[u] ? it : 0;
+      const int g = itc / kCols;
+      c4[u] = (itc % kCols) * 4;
+      row[u] = ((long long)b * a.Hq + h * a.G + g) * a.S;
     }
-    a.out[((long long)b * a.Hq + h * a.G + g) * D + dim] =
-        (_Float16)(den > 0.0f ? num / den : 0.0f);
+    float M[2] = {-INFINITY, -INFINITY}, den[2] = {0.0f, 0.0f};
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int i0 = 0; i0 < nparts; i0 += kParts) {
+      float l[2][kParts];
+      f32x4 o[2][kParts];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < kParts; ++j) {
+          const long long r = row[u] + min(i0 + j, nparts - 1);
+          l[u][j] = load_coherent(a.ws_lse + r);
+          const float2 lo = load_coherent2(a.ws_o + r * D + c4[u]);
+          const float2 hi = load_coherent2(a.ws_o + r * D + c4[u] + 2);
+          o[u][j] = f32x4{lo.x, lo.y, hi.x, hi.y};
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        float mc = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kParts; ++j) {
+          if (i0 + j >= nparts) l[u][j] = -INFINITY;
+          mc = fmaxf(mc, l[u][j]);
+        }
+        const float mn = fmaxf(M[u], mc);
+        if (mn == -INFINITY) continue;             // no tokens so far
+        const float sc = __builtin_amdgcn_exp2f((M[u] - mn) * kLog2e);
+        den[u] *= sc;
+        acc[u] *= sc;
+#pragma unroll
+        for (int j = 0; j < kParts; ++j) {
+          const float wj = __builtin_amdgcn_exp2f((l[u][j] - mn) * kLog2e);
+          den[u] += wj;
+          acc[u] += wj * o[u][j];
+        }
+        M[u] = mn;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (!live[u]) continue;
+      const float inv = den[u] > 0.0f ? 1.0f / den[u] : 0.0f;
+      const long long orow = row[u] / a.S;          // b * Hq + head
+      _Float16* out = a.out + orow * D + c4[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = (_Float16)(acc[u][e] * inv);
+    }
   }
 }
 
@@ -630,21 +696,25 @@ void decode_attn_stream_kernel(AttnArgs a) {
       st.write_rows(a, s.b, s.h, hw, -1, mrow, lg);
       return;
     }
-    st.write_rows(a, s.b, s.h, hw, slot, mrow, lg);
     if (a.mode == 2) {
+      st.write_rows(a, s.b, s.h, hw, slot, mrow, lg);
       if (s.t == s.n - 1 && hw == 0 && lane == 0)
         a.ws_count[(long long)s.b * a.Hkv + s.h] = slot + 1;
       return;
     }
-    // Publish the partial and count arrivals (NWH per worker); the last
-    // to arrive merges. The device-scope acquire-release atomic waits for
-    // this wave's partial stores and writes them back for the other XCDs,
-    // and for the merger drops stale cache lines before it reads.
+    // Publish the partial and count arrivals (NWH per worker); the last to
+    // arrive merges. The partial is written through with device-scope
+    // atomic stores; waiting for their completion before the counter update
+    // makes them visible to whichever compute unit merges, which reads them
+    // with device-scope atomic loads. (A release/acquire pair would instead
+    // write back and invalidate the whole L2 of the XCD at every arrival.)
+    st.template write_rows<true>(a, s.b, s.h, hw, slot, mrow, lg);
+    wait_vector_memory();
     int old = 0;
     if (lane == 0)
       old = __hip_atomic_fetch_add(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 1,
-                                   __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = uniform(__shfl(old, 0, 64));
     const int arrivals = (int)(last - first + 1) * NWH;
     if (old == arrivals - 1) {
       merge_partials<D>(a, s.b, s.h, (int)(last - first + 1), lane);

@@ -97,6 +97,29 @@ __device__ __forceinline__ T load_uniform(const T* p) {
       __builtin_bit_cast(unsigned long long, p));
 }
 
+// Device-scope relaxed atomic store / load of one float: on gfx950 a store
+// written through to the device-coherent level and a load served from it
+// (the per-XCD L2 caches are not coherent with each other).
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Two adjacent floats (8-byte aligned) in one device-scope atomic load.
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+  const unsigned long long v = __hip_atomic_load(
+      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED,
+      __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
+// Wait until every vector memory access this wave issued has completed
+// (s_waitcnt vmcnt(0); the other counters are left alone).
+__device__ __forceinline__ void wait_vector_memory() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
 __device__ __forceinline__ float read_lane(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }

@@ -270,11 +270,12 @@ int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
                                          int32_t max_context_len) {
   if (check_dims(dims) != PA_OK || max_context_len <= 0) return 1;
   // The split pass spreads the batch's 32-token tiles evenly over a
-  // persistent grid of W workgroups (512 for <= 16 q heads per kv head,
-  // else 256); the longest (sequence, kv head) then spans about
+  // persistent grid of W workers (2048 for <= 16 q heads per kv head, 1024
+  // for <= 32, else 512); the longest (sequence, kv head) then spans about
   // n_max * W / T + 1 of them. Assuming the batch's mean context is at
   // least 1/16 of the longest (T >= pairs * n_max / 16) gives the bound.
-  const long long W = dims->num_q_heads / dims->num_kv_heads <= 16 ? 512 : 256;
+  const int G = dims->num_q_heads / dims->num_kv_heads;
+  const long long W = G <= 16 ? 2048 : (G <= 32 ? 1024 : 512);
   const long long tiles = (max_context_len + 31) / 32;
   const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;
   if (tiles <= 1 || pairs <= 0) return 1;

@@ -93,21 +93,30 @@ struct TileRegs {
 // 8 * lg + 0..7 of the tile, all in block lg / 2: the V operand that P.V
 // needs is one run of 8 tokens. In a block's K storage rows 8 * m + 0..7
 // hold exactly MFMA m's tokens of that block.
+//
+// A dead load (live == false) keeps the load instructions, so that the
+// compiler's wait counts stay exact, but points all lanes of each
+// instruction at one line of the tile given by off0 (the tile just loaded):
+// 16 lines per wave instead of a whole tile re-read. (One shared address for
+// every wave would pile all waves' dead loads onto one memory channel.)
 template <int D, int BS, bool FP8>
 __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
                                           const uint8_t* kbase,
                                           const uint8_t* vbase, long long off0,
-                                          long long off1, int lane) {
+                                          long long off1, int lane, bool live) {
   using Gm = Geo<D, BS, FP8>;
   const int R = lane & 15, lg = lane >> 4;
-  const uint8_t* kb = kbase + (R < 8 ? off0 : off1) + (lg * 16 + (R & 7)) * 16;
+  if (!live) off1 = off0;
+  const int klane = live ? (lg * 16 + (R & 7)) * 16 : 0;
+  const int vlane = live ? ((lg & 1) * 16 + R) * 8 * Gm::kEsz : 0;
+  const uint8_t* kb = kbase + (R < 8 ? off0 : off1) + klane;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int jl = 0; jl < Gm::kKLoads; ++jl)
       t.k[m][jl] = __builtin_nontemporal_load(
           reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl));
-  const uint8_t* vb = vbase + (lg < 2 ? off0 : off1) + ((lg & 1) * 16 + R) * 8 * Gm::kEsz;
+  const uint8_t* vb = vbase + (lg < 2 ? off0 : off1) + vlane;
 #pragma unroll
   for (int jd = 0; jd < Gm::kPvMfma; ++jd)
     t.v[jd] = __builtin_nontemporal_load(
@@ -307,6 +316,11 @@ struct HeadState {
 __device__ __forceinline__ int uniform(int v) {
   return __builtin_amdgcn_readfirstlane(v);
 }
+__device__ __forceinline__ long long uniform(long long v) {
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)v);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(v >> 32));
+  return (long long)(((unsigned long long)hi << 32) | lo);
+}
 
 __device__ __forceinline__ int clamp_len(int L, int cap) {
   return L < 0 ? 0 : (L > cap ? cap : L);
@@ -338,7 +352,7 @@ void decode_attn_kernel(AttnArgs a) {
   using Smem = SharedMem<NH, NWH, TW, D>;
   __shared__ Smem sm;
   const int lane = threadIdx.x & 63;
-  const int wave = uniform(threadIdx.x >> 6);   // scalar: uniform control flow
+  const int wave = uniform((int)(threadIdx.x >> 6));   // scalar: uniform control flow
   const int hw = wave % NWH, tw = wave / NWH;
   const int mrow = lane & 15, lg = lane >> 4;
   const int h = blockIdx.x % a.Hkv;
@@ -363,29 +377,29 @@ void decode_attn_kernel(AttnArgs a) {
     const int ntiles = (ce - cs + kTile - 1) / kTile;
     const int last_blk = (ce - 1) & ~15;
     auto issue = [&](Tile& t, int k) {
-      const int ts = cs + k * kTile;
+      const bool live = k < ntiles;
+      const int ts = cs + (live ? k : 0) * kTile;
       long long off[2];
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const int tb = min(ts + 16 * r, last_blk);
         off[r] = sm.pages[tb / BS - p0] * page_stride + (tb % BS) * Gm::kRowBytes;
       }
-      load_tile<D, BS, FP8>(t, kbase, vbase, off[0], off[1], lane);
+      load_tile<D, BS, FP8>(t, kbase, vbase, off[0], off[1], lane, live);
     };
     // Two register tiles in flight; the next tile's loads are issued on
-    // every iteration, unconditionally (past the last tile they re-read the
-    // current one, already in L2), so the compiler waits only for the older
-    // tile's loads.
+    // every iteration, unconditionally (past the last tile as dead loads),
+    // so the compiler waits only for the older tile's loads.
     Tile ta, tb;
     int k = tw;
     if (k < ntiles) {
       issue(ta, k);
       while (true) {
-        issue(tb, k + TW < ntiles ? k + TW : k);
+        issue(tb, k + TW);
         st.compute(ta, cs + k * kTile, ce, lg);
         k += TW;
         if (k >= ntiles) break;
-        issue(ta, k + TW < ntiles ? k + TW : k);
+        issue(ta, k + TW);
         st.compute(tb, cs + k * kTile, ce, lg);
         k += TW;
         if (k >= ntiles) break;
@@ -507,6 +521,39 @@ __device__ __forceinline__ Cursor advance(const AttnArgs& a, Cursor c, int cap) 
   return c;
 }
 
+// The (sequence, kv head) pair holding global tile x of the split order
+// (0 <= x < total tiles): its sequence b, kv head h, tile t within it, its
+// tile count n and the global index of its first tile. Scalar results.
+__device__ __forceinline__ Cursor locate(const AttnArgs& a, long long x, int cap,
+                                         int lane) {
+  Cursor c{0, 0, 0, 1, 1, 0};
+  long long done = 0;                         // tiles (times Hkv) before chunk
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+    const int incl = wave_incl_sum(n, lane);
+    const long long lo = done + (long long)(incl - n) * a.Hkv;
+    const long long hi = done + (long long)incl * a.Hkv;
+    const unsigned long long hit = __ballot(x >= lo && x < hi);
+    if (hit) {
+      const int src = __ffsll((long long)hit) - 1;
+      c.b = c0 + src;
+      c.n = __shfl(n, src, 64);
+      const long long rel = x - __shfl(lo, src, 64);
+      c.h = (int)(rel / c.n);
+      c.t = (int)(rel % c.n);
+      break;
+    }
+    done += (long long)__shfl(incl, 63, 64) * a.Hkv;
+  }
+  c.b = uniform(c.b);
+  c.h = uniform(c.h);
+  c.t = uniform(c.t);
+  c.n = uniform(c.n);
+  c.L = clamp_len(load_uniform(a.context_lens + c.b), cap);
+  c.base = x - c.t;
+  return c;
+}
+
 // Byte offsets (head included) of the two 16-token blocks of c's tile. A
 // block wholly past the end re-reads the first one (in bounds; masked).
 template <int D, int BS, bool FP8>
@@ -529,23 +576,23 @@ __device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
 }
 
 // Merge the nparts partials of (b, h) from the workspace into out (fp16),
-// one wave: each lane owns 4 output values of one head for up to two heads
-// at a time and folds the partials in by an online log-sum-exp, the loads of
-// eight partials for both in flight together. The loads are device-scope
-// atomics, so they see the partials that other compute units wrote through
-// (write_rows<true>).
-template <int D>
+// one wave: each lane owns 4 output values of one head for up to ITEMS
+// heads at a time and folds the partials in by an online log-sum-exp, the
+// loads of PARTS partials for all of them in flight together. The loads are
+// device-scope atomics, so they see the partials that other compute units
+// wrote through (write_rows<true>).
+template <int D, int ITEMS, int PARTS>
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
                                                int nparts, int lane) {
   constexpr int kCols = D / 4;
-  constexpr int kParts = 8;
+  constexpr int kParts = PARTS;
   const int items = a.G * kCols;
-  for (int base = 0; base < items; base += 128) {
-    long long row[2];
-    int c4[2];
-    bool live[2];
+  for (int base = 0; base < items; base += 64 * ITEMS) {
+    long long row[ITEMS];
+    int c4[ITEMS];
+    bool live[ITEMS];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
       const int it = base + 64 * u + lane;
       live[u] = it < items;
       const int itc = live[u] ? it : 0;
@@ -553,13 +600,19 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
       c4[u] = (itc % kCols) * 4;
       row[u] = ((long long)b * a.Hq + h * a.G + g) * a.S;
     }
-    float M[2] = {-INFINITY, -INFINITY}, den[2] = {0.0f, 0.0f};
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int i0 = 0; i0 < nparts; i0 += kParts) {
-      float l[2][kParts];
-      f32x4 o[2][kParts];
+    float M[ITEMS], den[ITEMS];
+    f32x4 acc[ITEMS];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < ITEMS; ++u) {
+      M[u] = -INFINITY;
+      den[u] = 0.0f;
+      acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int i0 = 0; i0 < nparts; i0 += kParts) {
+      float l[ITEMS][kParts];
+      f32x4 o[ITEMS][kParts];
+#pragma unroll
+      for (int u = 0; u < ITEMS; ++u)
 #pragma unroll
         for (int j = 0; j < kParts; ++j) {
           const long long r = row[u] + min(i0 + j, nparts - 1);
@@ -569,7 +622,7 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
           o[u][j] = f32x4{lo.x, lo.y, hi.x, hi.y};
         }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < ITEMS; ++u) {
         float mc = -INFINITY;
 #pragma unroll
         for (int j = 0; j < kParts; ++j) {
@@ -591,7 +644,7 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
       }
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < ITEMS; ++u) {
       if (!live[u]) continue;
       const float inv = den[u] > 0.0f ? 1.0f / den[u] : 0.0f;
       const long long orow = row[u] / a.S;          // b * Hq + head
@@ -602,11 +655,15 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
   }
 }
 
-// Worker k (a wave, or NWH waves with head blocks split between them)
-// covers global tiles [k*tpw, (k+1)*tpw) of the sequence-major, then
-// kv-head-major, then token order, where each (sequence, kv head) has
-// ceil(L/32) tiles; tpw = max(ceil(T / workers), ceil(n_max / (S - 1)))
-// keeps every (sequence, kv head) within S partials. mode 2 writes the
+// Worker k (a wave, or NWH waves with head blocks split between them) of
+// W covers global tiles [floor(k T / W), floor((k + 1) T / W)) of the
+// sequence-major, then kv-head-major, then token order, where each
+// (sequence, kv head) has ceil(L/32) tiles and T is their total. Every
+// share thus has floor(T / W) or one more tiles; W is the grid's worker
+// count unless that would cut some (sequence, kv head) into more than S
+// ranges (checked exactly), in which case W is lowered until
+// floor(T / W) >= ceil(n_max / (S - 1)), which bounds every pair by S
+// ranges. mode 2 writes the
 // partials and their count; mode 3 merges too: a (sequence, kv head) held
 // by one worker is written out directly, otherwise the last of its workers
 // to finish (an atomic counter per (sequence, kv head), returned to zero
@@ -621,7 +678,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
   // the wave index in a scalar register, so that the worker's share, the
   // loop control and the block-table reads are scalar: a vector load of a
   // page id would have to wait for the tile loads issued before it
-  const int wave = uniform(threadIdx.x >> 6);
+  const int wave = uniform((int)(threadIdx.x >> 6));
   const int hw = wave % NWH;
   const int mrow = lane & 15, lg = lane >> 4;
   const int workers = gridDim.x * kWorkersPerWg;
@@ -638,10 +695,31 @@ void decode_attn_stream_kernel(AttnArgs a) {
   carry = uniform(carry);
   n_max = uniform(n_max);
   const long long T = (long long)carry * a.Hkv;
-  long long tpw = (T + workers - 1) / workers;
   const long long need = (n_max + (a.S - 1) - 1) / (a.S - 1);
-  if (tpw < need) tpw = need;
-  if (tpw < 1) tpw = 1;
+  // never more workers than tiles: every share holds at least one tile, so
+  // the workers between a pair's first and last owner all cover part of it
+  long long W = workers < T ? workers : T;     // (all of these are scalars)
+  if (need > 0 && T > 0 && T / need < W) {
+    // the quick bound fails at the full grid: count the ranges exactly
+    int worst = 0;
+    long long done = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+      const int incl = wave_incl_sum(n, lane);
+      if (n > 0) {
+        const long long x0 = done + (long long)(incl - n) * a.Hkv;
+        for (int h = 0; h < a.Hkv; ++h) {
+          const long long f = ((x0 + (long long)h * n + 1) * W - 1) / T;
+          const long long l = ((x0 + (long long)(h + 1) * n) * W - 1) / T;
+          worst = max(worst, (int)(l - f + 1));
+        }
+      }
+      done += (long long)__shfl(incl, 63, 64) * a.Hkv;
+    }
+    if (uniform(wave_max(worst)) > a.S) W = T / need;
+  }
+  if (W < 1) W = 1;
+  W = uniform(W);
 
   if (a.mode == 3 && hw == 0) {
     // sequences without tokens get zeros (no worker covers them)
@@ -651,46 +729,34 @@ void decode_attn_stream_kernel(AttnArgs a) {
         a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
     }
   }
-  const long long r0 = (long long)worker * tpw;
-  if (r0 >= T) return;                        // this wave has no share
-  const long long r1 = min(T, r0 + tpw);
+  if (worker >= W) return;                    // this wave has no share
+  const long long r0 = uniform((long long)worker * T / W);
+  const long long r1 = uniform((long long)(worker + 1) * T / W);
+  if (r0 >= r1) return;
 
-  // 2. the sequence, kv head and tile of global tile r0
-  Cursor c{0, 0, 0, 1, 1, 0};
+  // 2. the pairs holding this share's first and last tile. Only those two
+  // can extend past the share; the workers owning their far ends (tile x
+  // belongs to worker floor(((x + 1) W - 1) / T)) are worked out here, so
+  // the loop needs no division.
+  Cursor c = locate(a, r0, cap, lane);
+  long long fw = worker, lw = worker;
+  if (c.base < r0) fw = uniform(((c.base + 1) * W - 1) / T);
   {
-    long long done = 0;                       // tiles (times Hkv) before chunk
-    for (int c0 = 0; c0 < a.B; c0 += 64) {
-      const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
-      const int incl = wave_incl_sum(n, lane);
-      const long long lo = done + (long long)(incl - n) * a.Hkv;
-      const long long hi = done + (long long)incl * a.Hkv;
-      const unsigned long long hit = __ballot(r0 >= lo && r0 < hi);
-      if (hit) {
-        const int src = __ffsll((long long)hit) - 1;
-        c.b = c0 + src;
-        c.n = __shfl(n, src, 64);
-        const long long rel = r0 - __shfl(lo, src, 64);
-        c.h = (int)(rel / c.n);
-        c.t = (int)(rel % c.n);
-        break;
-      }
-      done += (long long)__shfl(incl, 63, 64) * a.Hkv;
-    }
+    const Cursor e = locate(a, r1 - 1, cap, lane);
+    if (e.base + e.n > r1) lw = uniform(((e.base + e.n) * W - 1) / T);
   }
-  c.b = uniform(c.b);
-  c.h = uniform(c.h);
-  c.t = uniform(c.t);
-  c.n = uniform(c.n);
-  c.L = clamp_len(load_uniform(a.context_lens + c.b), cap);
-  c.base = r0 - c.t;
 
   HeadState<D, BS, FP8, NH> st;
   st.begin(a, c.b, c.h, hw, mrow, lg);
 
   // End of (b, h)'s segment in this share: partial or output, and merge.
-  auto finish = [&](const Cursor& s) {
+  // (AT_END: the share's last pair, merged after the loop with the wider
+  // merge; inside the loop the narrow one keeps register pressure down.)
+  auto finish = [&](const Cursor& s, auto at_end) {
     st.reduce_sums();
-    const long long first = s.base / tpw, last = (s.base + s.n - 1) / tpw;
+    // workers owning the pair's first and last tile
+    const long long first = s.base < r0 ? fw : worker;
+    const long long last = s.base + s.n > r1 ? lw : worker;
     const int slot = (int)(worker - first);
     if (a.mode == 3 && first == last) {
       st.write_rows(a, s.b, s.h, hw, -1, mrow, lg);
@@ -717,7 +783,10 @@ void decode_attn_stream_kernel(AttnArgs a) {
     old = uniform(__shfl(old, 0, 64));
     const int arrivals = (int)(last - first + 1) * NWH;
     if (old == arrivals - 1) {
-      merge_partials<D>(a, s.b, s.h, (int)(last - first + 1), lane);
+      if constexpr (decltype(at_end)::value)
+        merge_partials<D, 2, 8>(a, s.b, s.h, (int)(last - first + 1), lane);
+      else
+        merge_partials<D, 1, 4>(a, s.b, s.h, (int)(last - first + 1), lane);
       if (lane == 0)
         __hip_atomic_store(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 0,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -729,21 +798,21 @@ void decode_attn_stream_kernel(AttnArgs a) {
   Tile ta, tb;
   long long o0, o1;
   tile_offsets<D, BS, FP8>(a, c, o0, o1);
-  load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane);
+  load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane, true);
   long long pos = r0;
   // One pipeline over the whole share: the next tile's loads (even in the
   // next segment) are in flight while the current tile is computed. They
-  // are issued unconditionally (past the share's end they re-read the
-  // current tile) so that the compiler waits only for the older tile.
+  // are issued unconditionally (past the share's end as dead loads) so
+  // that the compiler waits only for the older tile.
   while (true) {
     bool more = pos + 1 < r1;
     Cursor nx = more ? advance(a, c, cap) : c;
     tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-    load_tile<D, BS, FP8>(tb, kp, vp, o0, o1, lane);
+    load_tile<D, BS, FP8>(tb, kp, vp, o0, o1, lane, more);
     st.compute(ta, c.t * kTile, c.L, lg);
-    if (!more || nx.b != c.b || nx.h != c.h) {
-      finish(c);
-      if (!more) break;
+    if (!more) break;
+    if (nx.b != c.b || nx.h != c.h) {
+      finish(c, std::false_type{});
       st.begin(a, nx.b, nx.h, hw, mrow, lg);
     }
     ++pos;
@@ -752,16 +821,17 @@ void decode_attn_stream_kernel(AttnArgs a) {
     more = pos + 1 < r1;
     nx = more ? advance(a, c, cap) : c;
     tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-    load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane);
+    load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane, more);
     st.compute(tb, c.t * kTile, c.L, lg);
-    if (!more || nx.b != c.b || nx.h != c.h) {
-      finish(c);
-      if (!more) break;
+    if (!more) break;
+    if (nx.b != c.b || nx.h != c.h) {
+      finish(c, std::false_type{});
       st.begin(a, nx.b, nx.h, hw, mrow, lg);
     }
     ++pos;
     c = nx;
   }
+  finish(c, std::true_type{});
 }
 
 // ---------------------------------------------------------------------------

@@ -349,6 +349,48 @@ def test_decode_step_append_then_attend():
         assert max_err(gpu_decode(dw, 3), oracle_out(w)) <= TOL[kv_dtype]
 
 
+@pytest.mark.parametrize("shape", [(32, 8, 8), (48, 1, 8), (16, 2, 1)],
+                         ids=["merged-in-kernel", "split+reduce", "single-pass"])
+def test_graph_replay_matches_eager(shape):
+    """The decode step (kv_append + attention) captured as a HIP graph gives,
+    on every replay, the bits of the eager step, with other eager library
+    work and synchronisations between the replays."""
+    Hq, Hkv, S = shape
+    say("graph replay", shape)
+    pa = pa_mod()
+    w = make_case(6, Hq, Hkv, 128, 16, (1500, 1, 700, 64, 2100, 333), seed=303)
+    dw = DeviceWorkload(w, upto_last=True)
+    ws = pa.splitk_workspace(dw.q, dw.k_pages, dw.block_table, S)
+    out = torch.empty_like(dw.q)
+    stream = torch.cuda.Stream()
+
+    def step():
+        pa.kv_append(dw.new_k, dw.new_v, dw.k_pages, dw.v_pages, dw.block_table,
+                     dw.positions, stream=stream)
+        pa.paged_decode_attn_splitk_merged(dw.q, dw.k_pages, dw.v_pages, dw.block_table,
+                                           dw.context_lens, dw.scale, S, ws, out=out,
+                                           stream=stream)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    assert max_err(ref, oracle_out(w)) <= TOL["fp16"]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.zero_()
+        other = gpu_decode(dw, 3)          # eager library work in between
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i}"
+        assert torch.isfinite(other.float()).all()
+
+
 # -- full-size workloads, sampled ------------------------------------------
 
 FULL = {"tiny_mqa": None, "gqa_llama": (0, 7, 31), "wide_mqa": (0, 63),

@@ -76,7 +76,7 @@ CONFIGS = {
     # Llama-style GQA layer: batch 32, 32 q / 8 kv heads, d 128, pages of 16,
     # lengths uniform on [512, 4096].
     "gqa_llama": Config("gqa_llama", 32, 32, 8, 128, 16, "fp16", 1.0,
-                        ("uniform", 512, 4096), 4096, 16, seed=1002),
+                        ("uniform", 512, 4096), 4096, 32, seed=1002),
     # Wide MQA: batch 64, 96 q / 1 kv head, d 128, pages of 32, 8192 each,
     # values N(0, 0.5) (standard deviation 0.5).
     "wide_mqa": Config("wide_mqa", 64, 96, 1, 128, 32, "fp16", 0.5,

@@ -578,7 +578,8 @@ __device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
 // Merge the nparts partials of (b, h) from the workspace into out (fp16),
 // one wave: each lane owns 4 output values of one head for up to ITEMS
 // heads at a time and folds the partials in by an online log-sum-exp, the
-// loads of PARTS partials for all of them in flight together. The loads are
+// loads of PARTS partials for all of them in flight together. The rounding
+// depends on PARTS (one rescale per group), not on ITEMS. The loads are
 // device-scope atomics, so they see the partials that other compute units
 // wrote through (write_rows<true>).
 template <int D, int ITEMS, int PARTS>
@@ -750,8 +751,10 @@ void decode_attn_stream_kernel(AttnArgs a) {
   st.begin(a, c.b, c.h, hw, mrow, lg);
 
   // End of (b, h)'s segment in this share: partial or output, and merge.
-  // (AT_END: the share's last pair, merged after the loop with the wider
-  // merge; inside the loop the narrow one keeps register pressure down.)
+  // (AT_END: the share's last pair, merged after the loop two columns per
+  // lane at a time; inside the loop one column keeps register pressure
+  // down. Both fold the partials in the same groups of eight, so the result
+  // does not depend on which worker happens to arrive last.)
   auto finish = [&](const Cursor& s, auto at_end) {
     st.reduce_sums();
     // workers owning the pair's first and last tile
@@ -786,7 +789,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
       if constexpr (decltype(at_end)::value)
         merge_partials<D, 2, 8>(a, s.b, s.h, (int)(last - first + 1), lane);
       else
-        merge_partials<D, 1, 4>(a, s.b, s.h, (int)(last - first + 1), lane);
+        merge_partials<D, 1, 8>(a, s.b, s.h, (int)(last - first + 1), lane);
       if (lane == 0)
         __hip_atomic_store(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 0,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

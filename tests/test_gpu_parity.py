@@ -335,6 +335,10 @@ def test_repeated_calls_are_deterministic():
     a = [gpu_decode(dw).cpu() for _ in range(3)] + [gpu_decode(dw, 4).cpu() for _ in range(3)]
     assert all(torch.equal(a[0], x) for x in a[1:3])
     assert all(torch.equal(a[3], x) for x in a[4:6])
+    # the in-kernel merge: whichever worker arrives last, the same bits
+    m = [gpu_decode(dw, S, merged=True).cpu() for S in (4, 4, 4, 4, 4, 9, 9, 9, 9, 9)]
+    assert all(torch.equal(m[0], x) for x in m[1:5])
+    assert all(torch.equal(m[5], x) for x in m[6:])
 
 
 def test_decode_step_append_then_attend():

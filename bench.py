@@ -3,8 +3,9 @@
 
 A step is the whole hot path over one batch: kv_append of every sequence's
 new token into its page, then decode attention over the sequence's context
-(the split pass with its log-sum-exp merge, in one call, or the single pass
-when the workload uses one split). Inputs are seeded synthetic data already
+(the split pass with its log-sum-exp merge, or the single pass when the
+workload uses one split), issued as one paged_decode_step call: one kernel
+for groups of up to 16 q heads, the reduce kernel after it for wider ones. Inputs are seeded synthetic data already
 resident in HBM. R replicas of the KV pools rotate step to step so that the
 256 MB Infinity Cache cannot serve the working set. The R steps of one
 rotation (one per replica) are captured once as a HIP graph and replayed, as a
@@ -84,17 +85,20 @@ def measured_traffic(workload: str):
 
 
 def attention_algorithmic_bytes(w) -> int:
-    """Bytes decode attention must move at minimum: K/V of every attended
+    """Bytes one decode step must move at minimum: K/V of every attended
     token, q, the fp16 output, the block-table entries of those tokens, the
-    context lengths and (fp8) the scales. Split partials are this
-    implementation's overhead and are not counted."""
+    context lengths and positions, (fp8) the scales, and the appended rows
+    (fp16 in, cache format out). Split partials are this implementation's
+    overhead and are not counted."""
     cfg = w.cfg
     L = w.context_lens.astype("int64")
     nblk = -(-L // cfg.block_size)
     qb = cfg.num_seqs * cfg.num_q_heads * cfg.head_dim * 2
     scales = 0 if cfg.kv_dtype == "fp16" else 2 * cfg.num_kv_heads * 4
+    rows = cfg.num_seqs * cfg.num_kv_heads * cfg.head_dim * 2     # K and V
+    append = rows * 2 + rows * cfg.kv_bytes_per_elem
     return int(w.kv_bytes() + 2 * qb + int(nblk.sum()) * 4 * cfg.num_kv_heads
-               + cfg.num_seqs * 4 + scales)
+               + cfg.num_seqs * 8 + scales + append)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -186,21 +190,13 @@ def main():
     out = torch.empty_like(dw.q)
     group = cfg.num_q_heads // cfg.num_kv_heads
 
-    def append(r):
+    def step(r):
+        # kv_append + attention fused in one call (appending the same token
+        # again on later rotations writes the same bytes)
         kp, vp = pools[r]
-        pa.kv_append(dw.new_k, dw.new_v, kp, vp, dw.block_table, dw.positions,
-                     k_scale=dw.k_scale, v_scale=dw.v_scale, stream=stream)
-
-    def attention(r):
-        kp, vp = pools[r]
-        if S == 1:
-            pa.paged_decode_attn(dw.q, kp, vp, dw.block_table, dw.context_lens,
-                                 dw.scale, dw.k_scale, dw.v_scale, out=out, stream=stream)
-        else:
-            pa.paged_decode_attn_splitk_merged(dw.q, kp, vp, dw.block_table,
-                                               dw.context_lens, dw.scale, S, ws,
-                                               dw.k_scale, dw.v_scale, out=out,
-                                               stream=stream)
+        pa.paged_decode_step(dw.q, dw.new_k, dw.new_v, dw.positions, kp, vp,
+                             dw.block_table, dw.context_lens, dw.scale, S, ws,
+                             dw.k_scale, dw.v_scale, out=out, stream=stream)
 
     def capture(fn):
         g = torch.cuda.CUDAGraph()
@@ -211,12 +207,11 @@ def main():
     # eager run of every call once (first-use work stays out of the graphs)
     with torch.cuda.stream(stream):
         for r in range(R):
-            append(r)
-            attention(r)
+            step(r)
     torch.cuda.synchronize()
-    step_graphs = [capture(lambda r=r: (append(r), attention(r))) for r in range(R)]
-    rotation_graph = capture(lambda: [(append(r), attention(r)) for r in range(R)])
-    attn_graph = capture(lambda: [attention(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
+    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
+    rotation_graph = capture(lambda: [step(r) for r in range(R)])
+    attn_graph = capture(lambda: [step(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
     torch.cuda.synchronize()
 
     def run_steps(k):
@@ -238,8 +233,8 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
 
-    # attention launch duration: HIP events on the launch stream around
-    # replays of back-to-back attention launches (same rotation of pools)
+    # launch duration of the step's kernel: HIP events on the launch stream
+    # around replays of back-to-back launches (same rotation of pools)
     reps = max(4, args.steps // ATTN_LAUNCHES_PER_GRAPH)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -268,6 +263,7 @@ def main():
     else:
         attn_desc = "split pass + reduce kernel"
         kernel = "decode_attn_stream_kernel (+ splitk_reduce_kernel)"
+    attn_desc += ", kv_append fused into it"
     res = {
         "metric": METRIC,
         "value": round(value, 2),

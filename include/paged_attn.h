@@ -237,6 +237,36 @@ int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
                                     size_t workspace_bytes, void* out,
                                     hipStream_t stream);
 
+/*
+ * paged_decode_step — one decode step: kv_append of every sequence's new
+ * token, then paged_decode_attn_splitk_merged over the updated cache, with
+ * the append done inside the attention kernel (one launch for groups of at
+ * most 16 q heads; the reduce kernel follows for wider groups).
+ *
+ * Source: tiny-llm "优化", roadmap rows 分页 KV (the append is a scatter
+ * through the block table) and FlashDecoding, and section 5 (the append
+ * position of a decode step is a device value); "TensorRT对Multi-Query
+ * Attention的专项优化支持", decode paragraph (each step appends one K/V row
+ * per head and attends over all of them). Fusing the two is this library's.
+ *
+ * k_new, v_new: fp16 [B, Hkv, d] device; positions: int32 [B] device, the
+ * slot of sequence b's new token (normally context_lens[b] - 1; negative or
+ * beyond the table's capacity: no append). The result equals kv_append with
+ * seq_ids = NULL followed by paged_decode_attn_splitk_merged on the same
+ * arguments: the same cache bytes and the same output bits. The worker that
+ * reads the new token's tile writes it first, so no ordering is needed
+ * between sequences; a position inside the attended context other than its
+ * last token is allowed. Errors as paged_decode_attn_splitk_merged, plus
+ * PA_ERR_NULL for a missing k_new, v_new or positions.
+ */
+int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new,
+                      const void* v_new, const int32_t* positions,
+                      void* k_pages, void* v_pages, const int32_t* block_table,
+                      const int32_t* context_lens, float scale,
+                      const float* k_scale, const float* v_scale,
+                      int32_t num_splits, void* workspace,
+                      size_t workspace_bytes, void* out, hipStream_t stream);
+
 /* num_splits the library suggests for a batch whose longest context is
  * max_context_len tokens, assuming the batch's mean context is at least
  * 1/16 of the longest (1 when a single tile covers every context). */

@@ -20,6 +20,7 @@ __all__ = [
     "PaDims", "PagedAttnError", "KV_FP16", "KV_FP8_E4M3FN", "library_path",
     "load", "dims", "kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
     "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
+    "paged_decode_step",
     "splitk_workspace", "splitk_workspace_size",
     "suggest_splits", "status_string", "version",
 ]
@@ -68,6 +69,7 @@ def load():
         "paged_decode_attn_splitk": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P]),
         "paged_decode_attn_splitk_reduce": (I, [D, P, I, P, Z, P, P]),
         "paged_decode_attn_splitk_merged": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
+        "paged_decode_step": (I, [D, P, P, P, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
         "paged_decode_attn_suggest_splits": (I, [D, I]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_version": (I, []),
@@ -252,6 +254,29 @@ def paged_decode_attn_splitk_merged(q, k_pages, v_pages, block_table, context_le
         _ptr(context_lens), float(scale), _ptr(k_scale), _ptr(v_scale), int(num_splits),
         _ptr(workspace), nbytes, _ptr(out), _stream(stream))
     _check("paged_decode_attn_splitk_merged", rc)
+    return out
+
+
+def paged_decode_step(q, k_new, v_new, positions, k_pages, v_pages, block_table,
+                      context_lens, scale, num_splits, workspace, k_scale=None,
+                      v_scale=None, out=None, stream=None):
+    """kv_append of each sequence's new token (k_new/v_new [B, Hkv, d] fp16 at
+    positions [B]) and the merged split attention, fused; returns out."""
+    d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
+    _need(k_new, "k_new", torch.float16, 3)
+    _need(v_new, "v_new", torch.float16, 3)
+    _need(positions, "positions", torch.int32, 1)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float16, 3)
+    _need(workspace, "workspace")
+    nbytes = workspace.numel() * workspace.element_size()
+    rc = load().paged_decode_step(
+        ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions),
+        _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(context_lens),
+        float(scale), _ptr(k_scale), _ptr(v_scale), int(num_splits),
+        _ptr(workspace), nbytes, _ptr(out), _stream(stream))
+    _check("paged_decode_step", rc)
     return out
 
 

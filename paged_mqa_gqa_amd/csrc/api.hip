@@ -56,6 +56,20 @@ pa::AttnArgs make_args(const pa_dims* d, const void* q, const void* kp,
   return a;
 }
 
+// New tokens appended by the attention kernel itself (paged_decode_step).
+struct Fuse {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
+};
+
+void apply_fuse(pa::AttnArgs& a, const Fuse* f) {
+  if (!f) return;
+  a.k_new = static_cast<const _Float16*>(f->k_new);
+  a.v_new = static_cast<const _Float16*>(f->v_new);
+  a.positions = f->positions;
+}
+
 // Workspace: o f32 [B, Hq, S, D], lse f32 [B, Hq, S], count i32 [B, Hkv],
 // sem i32 [B, Hkv].
 size_t ws_bytes(const pa_dims* d, int32_t S) {
@@ -125,11 +139,13 @@ int kv_append(const pa_dims* dims, int32_t num_tokens, const void* k_new,
                                          stream));
 }
 
-int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
-                      const void* v_pages, const int32_t* block_table,
-                      const int32_t* context_lens, float scale,
-                      const float* k_scale, const float* v_scale, void* out,
-                      hipStream_t stream) {
+namespace {
+
+int single_impl(const pa_dims* dims, const void* q, const void* k_pages,
+                const void* v_pages, const int32_t* block_table,
+                const int32_t* context_lens, float scale, const float* k_scale,
+                const float* v_scale, void* out, hipStream_t stream,
+                const Fuse* fuse) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
@@ -143,8 +159,20 @@ int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
   a.out = static_cast<_Float16*>(out);
   a.S = 1;
   a.mode = 0;
+  apply_fuse(a, fuse);
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+}
+
+}  // namespace
+
+int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
+                      const void* v_pages, const int32_t* block_table,
+                      const int32_t* context_lens, float scale,
+                      const float* k_scale, const float* v_scale, void* out,
+                      hipStream_t stream) {
+  return single_impl(dims, q, k_pages, v_pages, block_table, context_lens,
+                     scale, k_scale, v_scale, out, stream, nullptr);
 }
 
 size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
@@ -154,13 +182,13 @@ size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
   return ws_bytes(dims, num_splits);
 }
 
-int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
-                             const void* k_pages, const void* v_pages,
-                             const int32_t* block_table,
-                             const int32_t* context_lens, float scale,
-                             const float* k_scale, const float* v_scale,
-                             int32_t num_splits, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+int split_impl(const pa_dims* dims, const void* q, const void* k_pages,
+               const void* v_pages, const int32_t* block_table,
+               const int32_t* context_lens, float scale, const float* k_scale,
+               const float* v_scale, int32_t num_splits, void* workspace,
+               size_t workspace_bytes, hipStream_t stream, const Fuse* fuse) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!q || !k_pages || !v_pages || !block_table || !context_lens)
@@ -182,22 +210,37 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
   a.ws_sem = v.sem;
   a.S = num_splits;
   a.mode = num_splits == 1 ? 1 : 2;
+  apply_fuse(a, fuse);
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+}
+
+}  // namespace
+
+int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
+                             const void* k_pages, const void* v_pages,
+                             const int32_t* block_table,
+                             const int32_t* context_lens, float scale,
+                             const float* k_scale, const float* v_scale,
+                             int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return split_impl(dims, q, k_pages, v_pages, block_table, context_lens, scale,
+                    k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                    stream, nullptr);
 }
 
 // Largest group size (q heads per kv head) whose partials the merged call
 // merges inside the attention kernel.
 constexpr int kMergeInKernelMaxGroup = 16;
 
-int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
-                                    const void* k_pages, const void* v_pages,
-                                    const int32_t* block_table,
-                                    const int32_t* context_lens, float scale,
-                                    const float* k_scale, const float* v_scale,
-                                    int32_t num_splits, void* workspace,
-                                    size_t workspace_bytes, void* out,
-                                    hipStream_t stream) {
+namespace {
+
+int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
+                const void* v_pages, const int32_t* block_table,
+                const int32_t* context_lens, float scale, const float* k_scale,
+                const float* v_scale, int32_t num_splits, void* workspace,
+                size_t workspace_bytes, void* out, hipStream_t stream,
+                const Fuse* fuse) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
@@ -209,16 +252,16 @@ int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
     return PA_ERR_SHAPE;
   if (dims->num_seqs == 0) return PA_OK;
   if (num_splits == 1)   // one range per (sequence, kv head): the single pass
-    return paged_decode_attn(dims, q, k_pages, v_pages, block_table,
-                             context_lens, scale, k_scale, v_scale, out, stream);
+    return single_impl(dims, q, k_pages, v_pages, block_table, context_lens,
+                       scale, k_scale, v_scale, out, stream, fuse);
   if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
     return PA_ERR_WORKSPACE;
   if (dims->num_q_heads / dims->num_kv_heads > kMergeInKernelMaxGroup) {
     // wide groups: one wave cannot merge G heads quickly; the reduce kernel
     // spreads the merge over a wave per (sequence, q head)
-    rc = paged_decode_attn_splitk(dims, q, k_pages, v_pages, block_table,
-                                  context_lens, scale, k_scale, v_scale,
-                                  num_splits, workspace, workspace_bytes, stream);
+    rc = split_impl(dims, q, k_pages, v_pages, block_table, context_lens, scale,
+                    k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                    stream, fuse);
     if (rc) return rc;
     return paged_decode_attn_splitk_reduce(dims, context_lens, num_splits,
                                            workspace, workspace_bytes, out, stream);
@@ -233,8 +276,40 @@ int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
   a.out = static_cast<_Float16*>(out);
   a.S = num_splits;
   a.mode = 3;
+  apply_fuse(a, fuse);
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
                                     dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+}
+
+}  // namespace
+
+int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
+                                    const void* k_pages, const void* v_pages,
+                                    const int32_t* block_table,
+                                    const int32_t* context_lens, float scale,
+                                    const float* k_scale, const float* v_scale,
+                                    int32_t num_splits, void* workspace,
+                                    size_t workspace_bytes, void* out,
+                                    hipStream_t stream) {
+  return merged_impl(dims, q, k_pages, v_pages, block_table, context_lens,
+                     scale, k_scale, v_scale, num_splits, workspace,
+                     workspace_bytes, out, stream, nullptr);
+}
+
+int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new,
+                      const void* v_new, const int32_t* positions,
+                      void* k_pages, void* v_pages, const int32_t* block_table,
+                      const int32_t* context_lens, float scale,
+                      const float* k_scale, const float* v_scale,
+                      int32_t num_splits, void* workspace,
+                      size_t workspace_bytes, void* out, hipStream_t stream) {
+  const int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!k_new || !v_new || !positions) return PA_ERR_NULL;
+  const Fuse f{k_new, v_new, positions};
+  return merged_impl(dims, q, k_pages, v_pages, block_table, context_lens,
+                     scale, k_scale, v_scale, num_splits, workspace,
+                     workspace_bytes, out, stream, &f);
 }
 
 int paged_decode_attn_splitk_reduce(const pa_dims* dims,
@@ -271,11 +346,11 @@ int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
   if (check_dims(dims) != PA_OK || max_context_len <= 0) return 1;
   // The split pass spreads the batch's 32-token tiles evenly over a
   // persistent grid of W workers (2048 for <= 16 q heads per kv head, 1024
-  // for <= 32, else 512); the longest (sequence, kv head) then spans about
+  // for <= 64, else 512); the longest (sequence, kv head) then spans about
   // n_max * W / T + 1 of them. Assuming the batch's mean context is at
   // least 1/16 of the longest (T >= pairs * n_max / 16) gives the bound.
   const int G = dims->num_q_heads / dims->num_kv_heads;
-  const long long W = G <= 16 ? 2048 : (G <= 32 ? 1024 : 512);
+  const long long W = G <= 16 ? 2048 : (G <= 64 ? 1024 : 512);
   const long long tiles = (max_context_len + 31) / 32;
   const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;
   if (tiles <= 1 || pairs <= 0) return 1;

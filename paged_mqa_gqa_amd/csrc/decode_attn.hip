@@ -124,12 +124,16 @@ __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
 }
 
 // Attention state of one wave for NH blocks of 16 q heads of one (sequence,
-// kv head), and the math of one tile.
-template <int D, int BS, bool FP8, int NH>
+// kv head), and the math of one tile. The q operands live in registers, or
+// with QL in this wave's LDS region `qsh` ([NH][d/32][64 lanes] of 16 bytes,
+// read back conflict-free), which leaves the registers to the accumulators
+// of wide groups.
+template <int D, int BS, bool FP8, int NH, bool QL = false>
 struct HeadState {
   using Gm = Geo<D, BS, FP8>;
   using Tile = TileRegs<D, BS, FP8>;
-  half8 qop[NH][Gm::kQkMfma];
+  half8 qop[QL ? 1 : NH][Gm::kQkMfma];
+  u32x4* qsh;
   float mrun[NH], lrun[NH];
   f32x4 acc[NH][Gm::kPvMfma];
   float sl, oscale;
@@ -153,7 +157,8 @@ struct HeadState {
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
         u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kslot_dim<FP8>(jj, lg));
         if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
-        qop[hb][jj] = as_half8(raw);
+        if constexpr (QL) qsh[(hb * Gm::kQkMfma + jj) * 64 + __lane_id()] = raw;
+        else qop[hb][jj] = as_half8(raw);
       }
       mrun[hb] = -INFINITY;
       lrun[hb] = 0.0f;
@@ -215,8 +220,11 @@ struct HeadState {
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
-        s0 = mfma_16x16x32(kop[0][jj], qop[hb][jj], s0);
-        s1 = mfma_16x16x32(kop[1][jj], qop[hb][jj], s1);
+        half8 qv;
+        if constexpr (QL) qv = as_half8(qsh[(hb * Gm::kQkMfma + jj) * 64 + __lane_id()]);
+        else qv = qop[hb][jj];
+        s0 = mfma_16x16x32(kop[0][jj], qv, s0);
+        s1 = mfma_16x16x32(kop[1][jj], qv, s1);
       }
       float sv[8];
 #pragma unroll
@@ -330,6 +338,30 @@ __device__ __forceinline__ int clamp_page(int p, int P) {
   return p < 0 ? 0 : (p >= P ? P - 1 : p);
 }
 
+// Fused append: write the new token of (sequence b, kv head h) at position p
+// into its page (one wave, two dimensions per lane), as kv_append does.
+template <int D, int BS, bool FP8>
+__device__ __forceinline__ void append_token(const AttnArgs& a, int b, int h,
+                                             int p, int lane) {
+  constexpr int kEsz = FP8 ? 1 : 2;
+  const int page = clamp_page(
+      load_uniform(a.block_table + (long long)b * a.max_blocks + p / BS), a.P);
+  const long long tile = ((long long)page * a.Hkv + h) * BS * D * kEsz;
+  uint8_t* kt = const_cast<uint8_t*>(a.k_pages) + tile;
+  uint8_t* vt = const_cast<uint8_t*>(a.v_pages) + tile;
+  const long long row = ((long long)b * a.Hkv + h) * D;
+  for (int dp = 2 * lane; dp < D; dp += 128) {
+    const uint32_t kin = *reinterpret_cast<const uint32_t*>(a.k_new + row + dp);
+    const uint32_t vin = *reinterpret_cast<const uint32_t*>(a.v_new + row + dp);
+    float ks = 1.0f, vs = 1.0f;
+    if constexpr (FP8) {
+      ks = load_uniform(a.k_scale + h);
+      vs = load_uniform(a.v_scale + h);
+    }
+    store_kv_pair<D, FP8>(kt, vt, p % BS, dp, kin, vin, ks, vs);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Single pass (or one split): one workgroup per (sequence, kv head); its
 // waves are NWH head-parallel groups times TW token-parallel waves whose
@@ -359,6 +391,16 @@ void decode_attn_kernel(AttnArgs a) {
   const int b = blockIdx.x / a.Hkv;
   const int L = clamp_len(load_uniform(a.context_lens + b), a.max_blocks * BS);
 
+  if (a.k_new != nullptr) {
+    // fused append before any tile is read; the barrier publishes it to the
+    // workgroup's other waves
+    if (wave == 0) {
+      const int p = load_uniform(a.positions + b);
+      if (p >= 0 && p < a.max_blocks * BS) append_token<D, BS, FP8>(a, b, h, p, lane);
+      wait_vector_memory();
+    }
+    __syncthreads();
+  }
   HeadState<D, BS, FP8, NH> st;
   st.begin(a, b, h, hw, mrow, lg);
   const uint8_t* kbase = a.k_pages + (long long)h * Gm::kPageBytes;
@@ -669,12 +711,15 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
 // by one worker is written out directly, otherwise the last of its workers
 // to finish (an atomic counter per (sequence, kv head), returned to zero
 // afterwards) merges the partials.
-template <int D, int BS, bool FP8, int NH, int NWH>
+template <int D, int BS, bool FP8, int NH, int NWH, bool QL>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_attn_stream_kernel(AttnArgs a) {
   using Tile = TileRegs<D, BS, FP8>;
+  using Gm = Geo<D, BS, FP8>;
   constexpr int kWorkersPerWg = 4 / NWH;
+  constexpr int kQWords = QL ? NH * Gm::kQkMfma * 64 : 1;   // 16 B each, per wave
+  __shared__ u32x4 qsmem[4][kQWords];
   const int lane = threadIdx.x & 63;
   // the wave index in a scalar register, so that the worker's share, the
   // loop control and the block-table reads are scalar: a vector load of a
@@ -722,12 +767,19 @@ void decode_attn_stream_kernel(AttnArgs a) {
   if (W < 1) W = 1;
   W = uniform(W);
 
-  if (a.mode == 3 && hw == 0) {
-    // sequences without tokens get zeros (no worker covers them)
+  if ((a.mode == 3 || a.k_new != nullptr) && hw == 0) {
+    // sequences without tokens: no worker covers them, so their zeros and
+    // their fused append are done here
     for (int b = worker; b < a.B; b += workers) {
       if (clamp_len(a.context_lens[b], cap) != 0) continue;
-      for (int i = lane; i < a.Hq * D; i += 64)
-        a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
+      if (a.mode == 3)
+        for (int i = lane; i < a.Hq * D; i += 64)
+          a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
+      if (a.k_new != nullptr) {
+        const int p = load_uniform(a.positions + b);
+        if (p >= 0 && p < cap)
+          for (int h = 0; h < a.Hkv; ++h) append_token<D, BS, FP8>(a, b, h, p, lane);
+      }
     }
   }
   if (worker >= W) return;                    // this wave has no share
@@ -740,15 +792,44 @@ void decode_attn_stream_kernel(AttnArgs a) {
   // belongs to worker floor(((x + 1) W - 1) / T)) are worked out here, so
   // the loop needs no division.
   Cursor c = locate(a, r0, cap, lane);
+  const Cursor e = locate(a, r1 - 1, cap, lane);
   long long fw = worker, lw = worker;
   if (c.base < r0) fw = uniform(((c.base + 1) * W - 1) / T);
-  {
-    const Cursor e = locate(a, r1 - 1, cap, lane);
-    if (e.base + e.n > r1) lw = uniform(((e.base + e.n) * W - 1) / T);
-  }
+  if (e.base + e.n > r1) lw = uniform(((e.base + e.n) * W - 1) / T);
 
-  HeadState<D, BS, FP8, NH> st;
-  st.begin(a, c.b, c.h, hw, mrow, lg);
+  HeadState<D, BS, FP8, NH, QL> st;
+  st.qsh = qsmem[wave];
+  st.begin(a, c.b, c.h, hw, mrow, lg);         // q loads overlap the append
+
+  if (a.k_new != nullptr) {
+    // Fused append: the worker whose share holds the tile of a pair's new
+    // token (its last tile if the position lies past the context) writes the
+    // token before loading any tile and waits for the stores, so its own
+    // loads of that tile see it. No other worker reads that tile; both
+    // waves of a two-wave worker write the same bytes. The share's first and
+    // last pairs are checked (their positions read together); pairs in
+    // between lie wholly inside the share.
+    auto append_if_here = [&](const Cursor& s, int p) {
+      if (p < 0 || p >= cap) return;
+      const long long tp = s.base + min(p / kTile, s.n - 1);
+      if (tp >= r0 && tp < r1) append_token<D, BS, FP8>(a, s.b, s.h, p, lane);
+    };
+    const int pc = load_uniform(a.positions + c.b);
+    const int pe = load_uniform(a.positions + e.b);
+    append_if_here(c, pc);
+    if (e.base != c.base) {
+      Cursor s = c;
+      s.t = s.n - 1;
+      s = advance(a, s, cap);                 // first tile of the next pair
+      while (s.base != e.base) {
+        append_if_here(s, load_uniform(a.positions + s.b));
+        s.t = s.n - 1;
+        s = advance(a, s, cap);
+      }
+      append_if_here(e, pe);
+    }
+    wait_vector_memory();
+  }
 
   // End of (b, h)'s segment in this share: partial or output, and merge.
   // (AT_END: the share's last pair, merged after the loop two columns per
@@ -841,27 +922,41 @@ void decode_attn_stream_kernel(AttnArgs a) {
 // Instances: head_dim {64, 128} x block_size {16, 32, 64} x {fp16, fp8} x
 // group-size class.
 template <int D, int BS, bool FP8, int NH, int NWH, int TW>
-static hipError_t launch_cfg(const AttnArgs& a, hipStream_t st) {
-  if (a.mode >= 2) {
-    // persistent grid: as many workgroups as fit at once on 256 CUs
-    constexpr int kPerCu = NH == 1 ? 2 : 1;
-    hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH>),
-                       256u * kPerCu, 256, 0, st, a);
-  } else {
-    const unsigned grid = (unsigned)((long long)a.B * a.Hkv);
-    hipLaunchKernelGGL((decode_attn_kernel<D, BS, FP8, NH, NWH, TW>), grid,
-                       64 * NWH * TW, 0, st, a);
-  }
+static hipError_t launch_single(const AttnArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)((long long)a.B * a.Hkv);
+  hipLaunchKernelGGL((decode_attn_kernel<D, BS, FP8, NH, NWH, TW>), grid,
+                     64 * NWH * TW, 0, st, a);
   return hipGetLastError();
 }
 
+// persistent grid: as many workgroups of 4 waves as fit at once on 256 CUs
+template <int D, int BS, bool FP8, int NH, int NWH, bool QL>
+static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
+  constexpr int kPerCu = NH == 1 ? 2 : 1;
+  hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH, QL>),
+                     256u * kPerCu, 256, 0, st, a);
+  return hipGetLastError();
+}
+
+// Group-size classes. Split pass: one wave streams each tile for up to 64
+// of the group's heads (q kept in LDS above 32), two waves (each with its
+// half of the heads) beyond; single pass: head-parallel and token-parallel
+// waves of one workgroup.
 template <int D, int BS, bool FP8>
 static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
-  if (a.G <= 16) return launch_cfg<D, BS, FP8, 1, 1, 4>(a, st);
-  if (a.G <= 32) return launch_cfg<D, BS, FP8, 2, 1, 4>(a, st);
-  if (a.G <= 64) return launch_cfg<D, BS, FP8, 2, 2, 2>(a, st);
-  if (a.G <= 96) return launch_cfg<D, BS, FP8, 3, 2, 2>(a, st);
-  if (a.G <= 128) return launch_cfg<D, BS, FP8, 4, 2, 2>(a, st);
+  if (a.mode >= 2) {
+    if (a.G <= 16) return launch_stream<D, BS, FP8, 1, 1, false>(a, st);
+    if (a.G <= 32) return launch_stream<D, BS, FP8, 2, 1, false>(a, st);
+    if (a.G <= 64) return launch_stream<D, BS, FP8, 4, 1, true>(a, st);
+    if (a.G <= 96) return launch_stream<D, BS, FP8, 3, 2, false>(a, st);
+    if (a.G <= 128) return launch_stream<D, BS, FP8, 4, 2, true>(a, st);
+    return hipErrorInvalidValue;
+  }
+  if (a.G <= 16) return launch_single<D, BS, FP8, 1, 1, 4>(a, st);
+  if (a.G <= 32) return launch_single<D, BS, FP8, 2, 1, 4>(a, st);
+  if (a.G <= 64) return launch_single<D, BS, FP8, 2, 2, 2>(a, st);
+  if (a.G <= 96) return launch_single<D, BS, FP8, 3, 2, 2>(a, st);
+  if (a.G <= 128) return launch_single<D, BS, FP8, 4, 2, 2>(a, st);
   return hipErrorInvalidValue;
 }
 

@@ -78,6 +78,40 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
   return sign | k;
 }
 
+// Store dims dp, dp+1 of one token's K and V rows (fp16 bits in kin / vin)
+// at slot `slot` of the (page, head) tiles ktile / vtile, in the page
+// layout: K rows of each 16-token block in 16-byte chunks with slots 4..7
+// and 8..11 swapped (bits 2 and 3 of the slot exchanged), V as runs of 8
+// tokens per dimension. fp8 tiles receive the e4m3fn codes of
+// value / scale (IEEE fp32 division, round to nearest even, saturating).
+template <int D, bool FP8>
+__device__ __forceinline__ void store_kv_pair(uint8_t* ktile, uint8_t* vtile,
+                                              int slot, int dp, uint32_t kin,
+                                              uint32_t vin, float ks, float vs) {
+  constexpr int X = FP8 ? 16 : 8;                     // elements per 16 B
+  const int blk = slot >> 4, r = slot & 15;
+  const int krow = (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
+  const int koff = ((blk * (D / X) + dp / X) * 16 + krow) * X + dp % X;
+  const int voff = (((blk * (D / 16) + dp / 16) * 2 + (r >> 3)) * 16 + dp % 16) * 8 + (r & 7);
+  if constexpr (!FP8) {
+    *reinterpret_cast<uint32_t*>(ktile + koff * 2) = kin;
+    uint16_t* vdst = reinterpret_cast<uint16_t*>(vtile) + voff;
+    vdst[0] = (uint16_t)(vin & 0xFFFFu);
+    vdst[8] = (uint16_t)(vin >> 16);
+  } else {
+    auto h2f = [](uint32_t bits) {
+      return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+    };
+    const uint32_t k0 = f32_to_e4m3fn(h2f(kin & 0xFFFFu) / ks);
+    const uint32_t k1 = f32_to_e4m3fn(h2f(kin >> 16) / ks);
+    const uint32_t v0 = f32_to_e4m3fn(h2f(vin & 0xFFFFu) / vs);
+    const uint32_t v1 = f32_to_e4m3fn(h2f(vin >> 16) / vs);
+    *reinterpret_cast<uint16_t*>(ktile + koff) = (uint16_t)(k0 | (k1 << 8));
+    vtile[voff] = (uint8_t)v0;
+    vtile[voff + 8] = (uint8_t)v1;
+  }
+}
+
 // Cross-lane exchange inside a wave (lane ^ mask), via ds_swizzle-free
 // bpermute: the address is in bytes.
 __device__ __forceinline__ float xor_lanes(float v, int mask) {

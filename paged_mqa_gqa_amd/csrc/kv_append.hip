@@ -34,35 +34,10 @@ __global__ __launch_bounds__(256) void kv_append_kernel(KvAppendArgs a) {
       a.k_new + (row * D + dp) * 2);
   const uint32_t vin = *reinterpret_cast<const uint32_t*>(
       a.v_new + (row * D + dp) * 2);
-  // element offsets inside the (page, head) tile (16-token blocks)
-  constexpr int X = FP8 ? 16 : 8;                     // elements per 16 B
-  const int blk = slot >> 4, r = slot & 15;
-  // K rows of a block: slots 4..7 and 8..11 trade places (bits 2, 3 swapped)
-  const int krow = (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
-  const long long tile = ((long long)page * a.Hkv + h) * a.bs * D;
-  const long long koff = tile + ((blk * (D / X) + dp / X) * 16 + krow) * X + dp % X;
-  const long long voff = tile + (((blk * (D / 16) + dp / 16) * 2 + (r >> 3)) * 16 +
-                                 dp % 16) * 8 + (r & 7);
-  if constexpr (!FP8) {
-    *reinterpret_cast<uint32_t*>(a.k_pages + koff * 2) = kin;
-    uint16_t* vdst = reinterpret_cast<uint16_t*>(a.v_pages) + voff;
-    vdst[0] = (uint16_t)(vin & 0xFFFFu);
-    vdst[8] = (uint16_t)(vin >> 16);
-  } else {
-    const float ks = a.k_scale[h];
-    const float vs = a.v_scale[h];
-    auto h2f = [](uint32_t bits) {
-      return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
-    };
-    // IEEE fp32 division (HIP's default float '/' is correctly rounded)
-    const uint32_t k0 = f32_to_e4m3fn(h2f(kin & 0xFFFFu) / ks);
-    const uint32_t k1 = f32_to_e4m3fn(h2f(kin >> 16) / ks);
-    const uint32_t v0 = f32_to_e4m3fn(h2f(vin & 0xFFFFu) / vs);
-    const uint32_t v1 = f32_to_e4m3fn(h2f(vin >> 16) / vs);
-    *reinterpret_cast<uint16_t*>(a.k_pages + koff) = (uint16_t)(k0 | (k1 << 8));
-    a.v_pages[voff] = (uint8_t)v0;
-    a.v_pages[voff + 8] = (uint8_t)v1;
-  }
+  const int esz = FP8 ? 1 : 2;
+  const long long tile = ((long long)page * a.Hkv + h) * a.bs * D * esz;
+  store_kv_pair<D, FP8>(a.k_pages + tile, a.v_pages + tile, slot, dp, kin, vin,
+                        FP8 ? a.k_scale[h] : 1.0f, FP8 ? a.v_scale[h] : 1.0f);
 }
 
 hipError_t launch_kv_append(const KvAppendArgs& a, int D, bool fp8,

@@ -32,6 +32,9 @@ struct AttnArgs {
   float* ws_lse;             // split pass: [B, Hq, S]
   int32_t* ws_count;         // split pass: [B, Hkv] partials per (b, h)
   int32_t* ws_sem;           // merged split pass: [B, Hkv] arrival counters
+  const _Float16* k_new;     // fused append (else null): [B, Hkv, D] fp16
+  const _Float16* v_new;
+  const int32_t* positions;  // [B] slot of the new token
   float scale_log2;          // scale * log2(e)
   int B, Hq, Hkv, G, P, max_blocks, S;
   int mode;                  // 0: single pass -> out; 1: one split per

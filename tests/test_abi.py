@@ -32,7 +32,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
               "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
-              "paged_decode_attn_splitk_workspace_size",
+              "paged_decode_step", "paged_decode_attn_splitk_workspace_size",
               "paged_decode_attn_suggest_splits", "pa_status_string", "pa_version"]:
         assert n in names
 
@@ -82,6 +82,25 @@ def test_null_pointers_rejected():
     assert attn(None) == -1
     for key in ["q", "k", "v", "bt", "lens", "out"]:
         assert attn(good_dims(), **{key: None}) == -1, key
+
+
+def test_decode_step_validation():
+    lib = pa.load()
+    d = good_dims()
+    need = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 4)
+
+    def step(dims=d, kn=FAKE, vn=FAKE, pos=FAKE, q=FAKE, S=4, ws=FAKE, n=need, out=FAKE):
+        return lib.paged_decode_step(ctypes.byref(dims) if dims is not None else None,
+                                     q, kn, vn, pos, FAKE, FAKE, FAKE, FAKE, 0.1,
+                                     None, None, S, ws, n, out, None)
+    assert step(dims=None) == -1
+    assert step(kn=None) == -1 and step(vn=None) == -1 and step(pos=None) == -1
+    assert step(q=None) == -1 and step(out=None) == -1
+    assert step(dims=good_dims(head_dim=96)) == -2
+    assert step(S=0) == -4
+    assert step(n=need - 1) == -5
+    assert step(dims=good_dims(kv_dtype=pa.KV_FP8_E4M3FN)) == -3
+    assert step(dims=good_dims(num_seqs=0)) == 0
 
 
 def test_fp8_requires_scales():

@@ -395,6 +395,38 @@ def test_graph_replay_matches_eager(shape):
         assert torch.isfinite(other.float()).all()
 
 
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("shape", [(32, 8, 16, 8), (48, 1, 32, 8), (16, 2, 16, 1),
+                                   (8, 2, 64, 3)],
+                         ids=["merged-in-kernel", "split+reduce", "single-pass", "bs64"])
+def test_fused_step_matches_append_then_merged(shape, kv_dtype):
+    """paged_decode_step gives the bits of kv_append followed by the merged
+    call: the same output and the same cache bytes (empty and one-token
+    contexts included)."""
+    Hq, Hkv, bs, S = shape
+    say("fused step", shape, kv_dtype)
+    pa = pa_mod()
+    lens = (1500, 1, 0, 700, 64, 2100, 333, 2)
+    w = make_case(len(lens), Hq, Hkv, 128, bs, lens, kv_dtype=kv_dtype, seed=304)
+    a = DeviceWorkload(w, upto_last=True)
+    b = DeviceWorkload(w, upto_last=True)
+    ws_a = pa.splitk_workspace(a.q, a.k_pages, a.block_table, S)
+    ws_b = pa.splitk_workspace(b.q, b.k_pages, b.block_table, S)
+    pa.kv_append(a.new_k, a.new_v, a.k_pages, a.v_pages, a.block_table, a.positions,
+                 k_scale=a.k_scale, v_scale=a.v_scale)
+    ref = pa.paged_decode_attn_splitk_merged(a.q, a.k_pages, a.v_pages, a.block_table,
+                                             a.context_lens, a.scale, S, ws_a,
+                                             a.k_scale, a.v_scale)
+    out = pa.paged_decode_step(b.q, b.new_k, b.new_v, b.positions, b.k_pages, b.v_pages,
+                               b.block_table, b.context_lens, b.scale, S, ws_b,
+                               b.k_scale, b.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k_pages.view(torch.uint8), b.k_pages.view(torch.uint8))
+    assert torch.equal(a.v_pages.view(torch.uint8), b.v_pages.view(torch.uint8))
+    assert torch.equal(out, ref)
+    assert max_err(out, oracle_out(w)) <= TOL[kv_dtype]
+
+
 # -- full-size workloads, sampled ------------------------------------------
 
 FULL = {"tiny_mqa": None, "gqa_llama": (0, 7, 31), "wide_mqa": (0, 63),

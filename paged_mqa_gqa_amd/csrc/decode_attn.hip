@@ -71,6 +71,12 @@ __device__ __forceinline__ int kslot_dim(int jj, int g) {
   return FP8 ? 64 * (jj >> 1) + 16 * g + 8 * (jj & 1) : 32 * jj + 8 * g;
 }
 
+template <bool NT, typename T>
+__device__ __forceinline__ T load16(const T* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 template <int D, int BS, bool FP8>
 struct TileRegs {
   using G = Geo<D, BS, FP8>;
@@ -83,8 +89,9 @@ struct TileRegs {
 
 // Issue the loads of one tile whose two 16-token blocks start at byte
 // offsets off0 / off1 of the K and V pools (head offset included). K/V are
-// read once per call, so the loads are nontemporal (streamed past the
-// caches' retention).
+// read once per call, so the loads are nontemporal (NT: streamed past the
+// caches' retention), except where two waves read the same tile one after
+// the other and the second should find it in the cache.
 //
 // Token order inside the tile: QK MFMA m (0, 1) takes as its 16 A rows the
 // tokens 8 * (R / 4) + 4 * m + R % 4 (R = 0..15), i.e. rows 0..7 from block
@@ -99,7 +106,7 @@ struct TileRegs {
 // instruction at one line of the tile given by off0 (the tile just loaded):
 // 16 lines per wave instead of a whole tile re-read. (One shared address for
 // every wave would pile all waves' dead loads onto one memory channel.)
-template <int D, int BS, bool FP8>
+template <int D, int BS, bool FP8, bool NT>
 __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
                                           const uint8_t* kbase,
                                           const uint8_t* vbase, long long off0,
@@ -114,12 +121,11 @@ __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int jl = 0; jl < Gm::kKLoads; ++jl)
-      t.k[m][jl] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl));
+      t.k[m][jl] = load16<NT>(reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl));
   const uint8_t* vb = vbase + (lg < 2 ? off0 : off1) + vlane;
 #pragma unroll
   for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-    t.v[jd] = __builtin_nontemporal_load(
+    t.v[jd] = load16<NT>(
         reinterpret_cast<const typename TileRegs<D, BS, FP8>::VT*>(vb + jd * 256 * Gm::kEsz));
 }
 
@@ -427,7 +433,7 @@ void decode_attn_kernel(AttnArgs a) {
         const int tb = min(ts + 16 * r, last_blk);
         off[r] = sm.pages[tb / BS - p0] * page_stride + (tb % BS) * Gm::kRowBytes;
       }
-      load_tile<D, BS, FP8>(t, kbase, vbase, off[0], off[1], lane, live);
+      load_tile<D, BS, FP8, NWH == 1>(t, kbase, vbase, off[0], off[1], lane, live);
     };
     // Two register tiles in flight; the next tile's loads are issued on
     // every iteration, unconditionally (past the last tile as dead loads),
@@ -619,16 +625,16 @@ __device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
 
 // Merge the nparts partials of (b, h) from the workspace into out (fp16),
 // one wave: each lane owns 4 output values of one head for up to ITEMS
-// heads at a time and folds the partials in by an online log-sum-exp, the
-// loads of PARTS partials for all of them in flight together. The rounding
-// depends on PARTS (one rescale per group), not on ITEMS. The loads are
-// device-scope atomics, so they see the partials that other compute units
-// wrote through (write_rows<true>).
-template <int D, int ITEMS, int PARTS>
+// heads at a time and folds the partials in by an online log-sum-exp, in
+// groups of 8 (one rescale per group: the rounding depends on the grouping
+// only, so every variant gives the same bits). The loads are device-scope
+// atomics, so they see the partials that other compute units wrote through
+// (write_rows<true>).
+template <int D, int ITEMS>
 __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
                                                int nparts, int lane) {
   constexpr int kCols = D / 4;
-  constexpr int kParts = PARTS;
+  constexpr int kParts = 8;
   const int items = a.G * kCols;
   for (int base = 0; base < items; base += 64 * ITEMS) {
     long long row[ITEMS];
@@ -651,9 +657,10 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
       den[u] = 0.0f;
       acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int i0 = 0; i0 < nparts; i0 += kParts) {
-      float l[ITEMS][kParts];
-      f32x4 o[ITEMS][kParts];
+    float l[ITEMS][kParts];
+    f32x4 o[ITEMS][kParts];
+    // loads of group i0 (past the last partial: re-reads of it)
+    auto fetch = [&](int i0) {
 #pragma unroll
       for (int u = 0; u < ITEMS; ++u)
 #pragma unroll
@@ -664,6 +671,8 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
           const float2 hi = load_coherent2(a.ws_o + r * D + c4[u] + 2);
           o[u][j] = f32x4{lo.x, lo.y, hi.x, hi.y};
         }
+    };
+    auto fold = [&](int i0) {
 #pragma unroll
       for (int u = 0; u < ITEMS; ++u) {
         float mc = -INFINITY;
@@ -685,6 +694,10 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
         }
         M[u] = mn;
       }
+    };
+    for (int i0 = 0; i0 < nparts; i0 += kParts) {
+      fetch(i0);
+      fold(i0);
     }
 #pragma unroll
     for (int u = 0; u < ITEMS; ++u) {
@@ -712,14 +725,15 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
 // to finish (an atomic counter per (sequence, kv head), returned to zero
 // afterwards) merges the partials.
 template <int D, int BS, bool FP8, int NH, int NWH, bool QL>
-__global__ __launch_bounds__(256)
+__global__ __launch_bounds__(NH == 1 ? 512 : 256)
 __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_attn_stream_kernel(AttnArgs a) {
   using Tile = TileRegs<D, BS, FP8>;
   using Gm = Geo<D, BS, FP8>;
-  constexpr int kWorkersPerWg = 4 / NWH;
+  constexpr int kWaves = NH == 1 ? 8 : 4;
+  constexpr int kWorkersPerWg = kWaves / NWH;
   constexpr int kQWords = QL ? NH * Gm::kQkMfma * 64 : 1;   // 16 B each, per wave
-  __shared__ u32x4 qsmem[4][kQWords];
+  __shared__ u32x4 qsmem[kWaves][kQWords];
   const int lane = threadIdx.x & 63;
   // the wave index in a scalar register, so that the worker's share, the
   // loop control and the block-table reads are scalar: a vector load of a
@@ -868,9 +882,9 @@ void decode_attn_stream_kernel(AttnArgs a) {
     const int arrivals = (int)(last - first + 1) * NWH;
     if (old == arrivals - 1) {
       if constexpr (decltype(at_end)::value)
-        merge_partials<D, 2, 8>(a, s.b, s.h, (int)(last - first + 1), lane);
+        merge_partials<D, 2>(a, s.b, s.h, (int)(last - first + 1), lane);
       else
-        merge_partials<D, 1, 8>(a, s.b, s.h, (int)(last - first + 1), lane);
+        merge_partials<D, 1>(a, s.b, s.h, (int)(last - first + 1), lane);
       if (lane == 0)
         __hip_atomic_store(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 0,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -882,7 +896,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
   Tile ta, tb;
   long long o0, o1;
   tile_offsets<D, BS, FP8>(a, c, o0, o1);
-  load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane, true);
+  load_tile<D, BS, FP8, NWH == 1>(ta, kp, vp, o0, o1, lane, true);
   long long pos = r0;
   // One pipeline over the whole share: the next tile's loads (even in the
   // next segment) are in flight while the current tile is computed. They
@@ -892,7 +906,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     bool more = pos + 1 < r1;
     Cursor nx = more ? advance(a, c, cap) : c;
     tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-    load_tile<D, BS, FP8>(tb, kp, vp, o0, o1, lane, more);
+    load_tile<D, BS, FP8, NWH == 1>(tb, kp, vp, o0, o1, lane, more);
     st.compute(ta, c.t * kTile, c.L, lg);
     if (!more) break;
     if (nx.b != c.b || nx.h != c.h) {
@@ -905,7 +919,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     more = pos + 1 < r1;
     nx = more ? advance(a, c, cap) : c;
     tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-    load_tile<D, BS, FP8>(ta, kp, vp, o0, o1, lane, more);
+    load_tile<D, BS, FP8, NWH == 1>(ta, kp, vp, o0, o1, lane, more);
     st.compute(tb, c.t * kTile, c.L, lg);
     if (!more) break;
     if (nx.b != c.b || nx.h != c.h) {
@@ -932,9 +946,8 @@ static hipError_t launch_single(const AttnArgs& a, hipStream_t st) {
 // persistent grid: as many workgroups of 4 waves as fit at once on 256 CUs
 template <int D, int BS, bool FP8, int NH, int NWH, bool QL>
 static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
-  constexpr int kPerCu = NH == 1 ? 2 : 1;
   hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH, QL>),
-                     256u * kPerCu, 256, 0, st, a);
+                     256u, NH == 1 ? 512 : 256, 0, st, a);
   return hipGetLastError();
 }
 

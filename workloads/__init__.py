@@ -80,7 +80,7 @@ CONFIGS = {
     # Wide MQA: batch 64, 96 q / 1 kv head, d 128, pages of 32, 8192 each,
     # values N(0, 0.5) (standard deviation 0.5).
     "wide_mqa": Config("wide_mqa", 64, 96, 1, 128, 32, "fp16", 0.5,
-                       ("const", 8192), 8192, 8, seed=1003),
+                       ("const", 8192), 8192, 16, seed=1003),
     # Long-context split-K: batch 4, 32 q / 8 kv heads, d 128, pages of 64,
     # 131072 tokens each, 64 splits merged by log-sum-exp.
     "long_splitk": Config("long_splitk", 4, 32, 8, 128, 64, "fp16", 1.0,

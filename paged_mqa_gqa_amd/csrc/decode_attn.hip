@@ -50,6 +50,7 @@
 namespace pa {
 
 constexpr int kTile = 32;       // tokens per tile
+constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax rescale
 constexpr int kMaxPages = 512;  // page ids staged in LDS per chunk (single pass)
 
 template <int D, int BS, bool FP8>
@@ -248,8 +249,14 @@ struct HeadState {
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
       mt = fmaxf(mt, xor_lanes(mt, 16));
       mt = fmaxf(mt, xor_lanes(mt, 32));
-      const float mn = fmaxf(mrun[hb], mt);
-      const float alpha = __builtin_amdgcn_exp2f(mrun[hb] - mn);
+      // Lazy rescale: the reference max mrun moves only when the tile's max
+      // exceeds it by more than kLazyLog2, so probabilities stay <= 2^8
+      // (fp16 P and the fp32 sums keep their relative precision) and the
+      // accumulators are rescaled a handful of times per segment instead of
+      // whenever the max grows. acc / l and m + log2(l) are unchanged.
+      const bool bump = mt > mrun[hb] + kLazyLog2;   // first tile: mrun = -inf
+      const float mn = bump ? mt : mrun[hb];
+      const float alpha = bump ? __builtin_amdgcn_exp2f(mrun[hb] - mt) : 1.0f;
       mrun[hb] = mn;
       float ps = 0.0f;
       half8 pop;
@@ -724,7 +731,7 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
 // by one worker is written out directly, otherwise the last of its workers
 // to finish (an atomic counter per (sequence, kv head), returned to zero
 // afterwards) merges the partials.
-template <int D, int BS, bool FP8, int NH, int NWH, bool QL>
+template <int D, int BS, bool FP8, int NH, int NWH, bool QL, int SLOTS>
 __global__ __launch_bounds__(NH == 1 ? 512 : 256)
 __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_attn_stream_kernel(AttnArgs a) {
@@ -893,41 +900,62 @@ void decode_attn_stream_kernel(AttnArgs a) {
 
   const uint8_t* kp = a.k_pages;
   const uint8_t* vp = a.v_pages;
-  Tile ta, tb;
   long long o0, o1;
-  tile_offsets<D, BS, FP8>(a, c, o0, o1);
-  load_tile<D, BS, FP8, NWH == 1>(ta, kp, vp, o0, o1, lane, true);
   long long pos = r0;
-  // One pipeline over the whole share: the next tile's loads (even in the
-  // next segment) are in flight while the current tile is computed. They
-  // are issued unconditionally (past the share's end as dead loads) so
-  // that the compiler waits only for the older tile.
-  while (true) {
-    bool more = pos + 1 < r1;
-    Cursor nx = more ? advance(a, c, cap) : c;
-    tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-    load_tile<D, BS, FP8, NWH == 1>(tb, kp, vp, o0, o1, lane, more);
-    st.compute(ta, c.t * kTile, c.L, lg);
-    if (!more) break;
-    if (nx.b != c.b || nx.h != c.h) {
-      finish(c, std::false_type{});
-      st.begin(a, nx.b, nx.h, hw, mrow, lg);
+  constexpr bool kNT = NWH == 1;
+  if constexpr (SLOTS == 2) {
+    Tile ta, tb;
+    tile_offsets<D, BS, FP8>(a, c, o0, o1);
+    load_tile<D, BS, FP8, kNT>(ta, kp, vp, o0, o1, lane, true);
+    // One pipeline over the whole share: the next tile's loads (even in the
+    // next segment) are in flight while the current tile is computed. They
+    // are issued unconditionally (past the share's end as dead loads) so
+    // that the compiler waits only for the older tile.
+    auto iter = [&](Tile& cur, Tile& nxt) {
+      const bool more = pos + 1 < r1;
+      const Cursor nx = more ? advance(a, c, cap) : c;
+      tile_offsets<D, BS, FP8>(a, nx, o0, o1);
+      load_tile<D, BS, FP8, kNT>(nxt, kp, vp, o0, o1, lane, more);
+      st.compute(cur, c.t * kTile, c.L, lg);
+      if (!more) return false;
+      if (nx.b != c.b || nx.h != c.h) {
+        finish(c, std::false_type{});
+        st.begin(a, nx.b, nx.h, hw, mrow, lg);
+      }
+      ++pos;
+      c = nx;
+      return true;
+    };
+    while (iter(ta, tb) && iter(tb, ta)) {
     }
-    ++pos;
-    c = nx;
-
-    more = pos + 1 < r1;
-    nx = more ? advance(a, c, cap) : c;
-    tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-    load_tile<D, BS, FP8, NWH == 1>(ta, kp, vp, o0, o1, lane, more);
-    st.compute(tb, c.t * kTile, c.L, lg);
-    if (!more) break;
-    if (nx.b != c.b || nx.h != c.h) {
-      finish(c, std::false_type{});
-      st.begin(a, nx.b, nx.h, hw, mrow, lg);
+  } else {
+    // Three register tiles: the loads of the two tiles after the current one
+    // are in flight while it is computed (wide groups, where each tile takes
+    // longest to compute).
+    Tile t0, t1, t2;
+    Cursor n1 = pos + 1 < r1 ? advance(a, c, cap) : c;
+    tile_offsets<D, BS, FP8>(a, c, o0, o1);
+    load_tile<D, BS, FP8, kNT>(t0, kp, vp, o0, o1, lane, true);
+    tile_offsets<D, BS, FP8>(a, n1, o0, o1);
+    load_tile<D, BS, FP8, kNT>(t1, kp, vp, o0, o1, lane, pos + 1 < r1);
+    auto iter = [&](Tile& cur, Tile& ld) {
+      const bool more2 = pos + 2 < r1;
+      const Cursor n2 = more2 ? advance(a, n1, cap) : n1;
+      tile_offsets<D, BS, FP8>(a, n2, o0, o1);
+      load_tile<D, BS, FP8, kNT>(ld, kp, vp, o0, o1, lane, more2);
+      st.compute(cur, c.t * kTile, c.L, lg);
+      if (pos + 1 >= r1) return false;
+      if (n1.b != c.b || n1.h != c.h) {
+        finish(c, std::false_type{});
+        st.begin(a, n1.b, n1.h, hw, mrow, lg);
+      }
+      ++pos;
+      c = n1;
+      n1 = n2;
+      return true;
+    };
+    while (iter(t0, t2) && iter(t1, t0) && iter(t2, t1)) {
     }
-    ++pos;
-    c = nx;
   }
   finish(c, std::true_type{});
 }
@@ -944,9 +972,9 @@ static hipError_t launch_single(const AttnArgs& a, hipStream_t st) {
 }
 
 // persistent grid: as many workgroups of 4 waves as fit at once on 256 CUs
-template <int D, int BS, bool FP8, int NH, int NWH, bool QL>
+template <int D, int BS, bool FP8, int NH, int NWH, bool QL, int SLOTS = 2>
 static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH, QL>),
+  hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH, QL, SLOTS>),
                      256u, NH == 1 ? 512 : 256, 0, st, a);
   return hipGetLastError();
 }

@@ -345,12 +345,14 @@ int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
                                          int32_t max_context_len) {
   if (check_dims(dims) != PA_OK || max_context_len <= 0) return 1;
   // The split pass spreads the batch's 32-token tiles evenly over a
-  // persistent grid of W workers (2048 for <= 16 q heads per kv head, 1024
-  // for <= 64, else 512); the longest (sequence, kv head) then spans about
+  // persistent grid of W workers (<= 16 q heads per kv head: 1024 for fp16,
+  // 2048 for fp8; 1024 up to 64; else 512); the longest (sequence, kv head)
+  // then spans about
   // n_max * W / T + 1 of them. Assuming the batch's mean context is at
   // least 1/16 of the longest (T >= pairs * n_max / 16) gives the bound.
   const int G = dims->num_q_heads / dims->num_kv_heads;
-  const long long W = G <= 16 ? 2048 : (G <= 64 ? 1024 : 512);
+  const long long W = G <= 16 ? (dims->kv_dtype == PA_KV_FP8_E4M3FN ? 2048 : 1024)
+                              : (G <= 64 ? 1024 : 512);
   const long long tiles = (max_context_len + 31) / 32;
   const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;
   if (tiles <= 1 || pairs <= 0) return 1;

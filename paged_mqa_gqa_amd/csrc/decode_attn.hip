@@ -732,12 +732,14 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
 // to finish (an atomic counter per (sequence, kv head), returned to zero
 // afterwards) merges the partials.
 template <int D, int BS, bool FP8, int NH, int NWH, bool QL, int SLOTS>
-__global__ __launch_bounds__(NH == 1 ? 512 : 256)
-__attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
+__global__ __launch_bounds__(NH == 1 && SLOTS == 2 ? 512 : 256)
+__attribute__((amdgpu_waves_per_eu(NH == 1 && SLOTS == 2 ? 2 : 1)))
 void decode_attn_stream_kernel(AttnArgs a) {
   using Tile = TileRegs<D, BS, FP8>;
   using Gm = Geo<D, BS, FP8>;
-  constexpr int kWaves = NH == 1 ? 8 : 4;
+  // one 8-wave workgroup per CU (two waves per SIMD) for the small
+  // two-tile configuration, else one wave per SIMD
+  constexpr int kWaves = NH == 1 && SLOTS == 2 ? 8 : 4;
   constexpr int kWorkersPerWg = kWaves / NWH;
   constexpr int kQWords = QL ? NH * Gm::kQkMfma * 64 : 1;   // 16 B each, per wave
   __shared__ u32x4 qsmem[kWaves][kQWords];
@@ -930,8 +932,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     }
   } else {
     // Three register tiles: the loads of the two tiles after the current one
-    // are in flight while it is computed (wide groups, where each tile takes
-    // longest to compute).
+    // are in flight while it is computed.
     Tile t0, t1, t2;
     Cursor n1 = pos + 1 < r1 ? advance(a, c, cap) : c;
     tile_offsets<D, BS, FP8>(a, c, o0, o1);
@@ -975,18 +976,24 @@ static hipError_t launch_single(const AttnArgs& a, hipStream_t st) {
 template <int D, int BS, bool FP8, int NH, int NWH, bool QL, int SLOTS = 2>
 static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH, QL, SLOTS>),
-                     256u, NH == 1 ? 512 : 256, 0, st, a);
+                     256u, NH == 1 && SLOTS == 2 ? 512 : 256, 0, st, a);
   return hipGetLastError();
 }
 
 // Group-size classes. Split pass: one wave streams each tile for up to 64
 // of the group's heads (q kept in LDS above 32), two waves (each with its
 // half of the heads) beyond; single pass: head-parallel and token-parallel
-// waves of one workgroup.
+// waves of one workgroup. (Workers: 1024 for fp16 groups of up to 16 heads,
+// 2048 for fp8 ones, 1024 up to 64 heads, 512 beyond.)
 template <int D, int BS, bool FP8>
 static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
   if (a.mode >= 2) {
-    if (a.G <= 16) return launch_stream<D, BS, FP8, 1, 1, false>(a, st);
+    // up to 16 heads: fp16 tiles run one wave per SIMD with three tiles in
+    // flight; fp8 tiles (half the bytes) two waves per SIMD with two each
+    if (a.G <= 16) {
+      if constexpr (FP8) return launch_stream<D, BS, FP8, 1, 1, false, 2>(a, st);
+      else return launch_stream<D, BS, FP8, 1, 1, false, 3>(a, st);
+    }
     if (a.G <= 32) return launch_stream<D, BS, FP8, 2, 1, false>(a, st);
     if (a.G <= 64) return launch_stream<D, BS, FP8, 4, 1, true>(a, st);
     if (a.G <= 96) return launch_stream<D, BS, FP8, 3, 2, false>(a, st);

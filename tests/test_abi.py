@@ -160,10 +160,12 @@ def test_status_strings_and_version():
 
 
 def test_suggest_splits():
-    d = pa.PaDims(256, 64, 8, 128, 16, 30000, 2048, pa.KV_FP16)
+    d = pa.PaDims(256, 64, 8, 128, 16, 30000, 2048, pa.KV_FP8_E4M3FN)
     assert pa.suggest_splits(d, 32768) == 17       # 16*2048/2048 + 1
+    d1 = pa.PaDims(256, 64, 8, 128, 16, 30000, 2048, pa.KV_FP16)
+    assert pa.suggest_splits(d1, 32768) == 9       # 16*1024/2048 + 1
     d2 = pa.PaDims(32, 32, 8, 128, 16, 5000, 256, pa.KV_FP16)
-    assert pa.suggest_splits(d2, 4096) == 64       # 16*2048/256 + 1, capped
+    assert pa.suggest_splits(d2, 4096) == 64       # 16*1024/256 + 1, capped
     d4 = pa.PaDims(4, 32, 8, 128, 64, 9000, 2048, pa.KV_FP16)
     assert pa.suggest_splits(d4, 131072) == 64      # capped
     assert pa.suggest_splits(d4, 1) == 1

@@ -427,6 +427,26 @@ def test_fused_step_matches_append_then_merged(shape, kv_dtype):
     assert max_err(out, oracle_out(w)) <= TOL[kv_dtype]
 
 
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("scale", [2.0, 4.0])
+def test_wide_score_range_exercises_the_rescale(scale, kv_dtype):
+    """Scores spread over tens of log2 units (softmax scale far above
+    1/sqrt(d)), so the running reference max of a head is bumped again and
+    again inside a segment: the accumulator rescale path, on every schedule."""
+    say("score range", scale, kv_dtype)
+    w = make_case(5, 32, 4, 128, 16, (3000, 97, 1, 640, 1500), kv_dtype=kv_dtype,
+                  seed=305, scale=scale)
+    dw = DeviceWorkload(w)
+    ref = oracle_out(w)
+    for S, merged in ((1, False), (6, False), (6, True), (33, True)):
+        err = max_err(gpu_decode(dw, S, merged=merged), ref)
+        assert err <= TOL[kv_dtype], (S, merged, err)
+    w2 = make_case(3, 96, 1, 128, 32, (2500, 33, 900), kv_dtype=kv_dtype, seed=306,
+                   scale=scale)                       # two-wave workers, reduce kernel
+    dw2 = DeviceWorkload(w2)
+    assert max_err(gpu_decode(dw2, 5, merged=True), oracle_out(w2)) <= TOL[kv_dtype]
+
+
 # -- full-size workloads, sampled ------------------------------------------
 
 FULL = {"tiny_mqa": None, "gqa_llama": (0, 7, 31), "wide_mqa": (0, 63),

@@ -859,7 +859,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
   // lane at a time; inside the loop one column keeps register pressure
   // down. Both fold the partials in the same groups of eight, so the result
   // does not depend on which worker happens to arrive last.)
-  auto finish = [&](const Cursor& s, auto at_end) {
+  auto finish = [&](const Cursor& s, auto at_end) __attribute__((always_inline)) {
     st.reduce_sums();
     // workers owning the pair's first and last tile
     const long long first = s.base < r0 ? fw : worker;

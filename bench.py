@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="override pool replicas")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--separate-append", action="store_true",
+                    help="issue kv_append and the attention call as two launches")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, --steps times")
     return ap.parse_args()
@@ -84,11 +86,12 @@ def measured_traffic(workload: str):
         return None
 
 
-def attention_algorithmic_bytes(w) -> int:
+def attention_algorithmic_bytes(w, with_append=True) -> int:
     """Bytes one decode step must move at minimum: K/V of every attended
     token, q, the fp16 output, the block-table entries of those tokens, the
     context lengths and positions, (fp8) the scales, and the appended rows
-    (fp16 in, cache format out). Split partials are this implementation's
+    (fp16 in, cache format out; left out with `with_append=False`, for the
+    attention launch alone). Split partials are this implementation's
     overhead and are not counted."""
     cfg = w.cfg
     L = w.context_lens.astype("int64")
@@ -97,6 +100,8 @@ def attention_algorithmic_bytes(w) -> int:
     scales = 0 if cfg.kv_dtype == "fp16" else 2 * cfg.num_kv_heads * 4
     rows = cfg.num_seqs * cfg.num_kv_heads * cfg.head_dim * 2     # K and V
     append = rows * 2 + rows * cfg.kv_bytes_per_elem
+    if not with_append:
+        append = 0
     return int(w.kv_bytes() + 2 * qb + int(nblk.sum()) * 4 * cfg.num_kv_heads
                + cfg.num_seqs * 8 + scales + append)
 
@@ -189,11 +194,28 @@ def main():
     ws = pa.splitk_workspace(dw.q, dw.k_pages, dw.block_table, S)
     out = torch.empty_like(dw.q)
     group = cfg.num_q_heads // cfg.num_kv_heads
+    # whether the library's step appends inside the attention kernel (it
+    # issues the append as a launch of its own for large pair counts)
+    fused = (pa.step_fuses_append(pa.dims(cfg.num_seqs, cfg.num_q_heads, dw.k_pages,
+                                          dw.block_table))
+             and not args.separate_append)
+
+    def attention(r):
+        kp, vp = pools[r]
+        pa.paged_decode_attn_splitk_merged(dw.q, kp, vp, dw.block_table,
+                                           dw.context_lens, dw.scale, S, ws,
+                                           dw.k_scale, dw.v_scale, out=out,
+                                           stream=stream)
 
     def step(r):
-        # kv_append + attention fused in one call (appending the same token
-        # again on later rotations writes the same bytes)
+        # kv_append + attention in one library call (appending the same
+        # token again on later rotations writes the same bytes)
         kp, vp = pools[r]
+        if args.separate_append:
+            pa.kv_append(dw.new_k, dw.new_v, kp, vp, dw.block_table, dw.positions,
+                         k_scale=dw.k_scale, v_scale=dw.v_scale, stream=stream)
+            attention(r)
+            return
         pa.paged_decode_step(dw.q, dw.new_k, dw.new_v, dw.positions, kp, vp,
                              dw.block_table, dw.context_lens, dw.scale, S, ws,
                              dw.k_scale, dw.v_scale, out=out, stream=stream)
@@ -211,7 +233,13 @@ def main():
     torch.cuda.synchronize()
     step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
     rotation_graph = capture(lambda: [step(r) for r in range(R)])
-    attn_graph = capture(lambda: [step(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
+    # the attention launch on its own: the step itself when the append is
+    # fused into it, else the attention call the step makes after its append
+    one = step if fused else attention
+    with torch.cuda.stream(stream):
+        one(0)
+    torch.cuda.synchronize()
+    attn_graph = capture(lambda: [one(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
     torch.cuda.synchronize()
 
     def run_steps(k):
@@ -248,7 +276,7 @@ def main():
     attn_avg_us = e0.elapsed_time(e1) * 1e3 / (reps * ATTN_LAUNCHES_PER_GRAPH)
 
     value = kvb / (ms_step * 1e-3) / 1e9
-    alg = attention_algorithmic_bytes(w)
+    alg = attention_algorithmic_bytes(w, with_append=fused)
     achieved = alg / (attn_avg_us * 1e-6) / 1e9
     traffic = measured_traffic(cfg.name)
 
@@ -263,7 +291,8 @@ def main():
     else:
         attn_desc = "split pass + reduce kernel"
         kernel = "decode_attn_stream_kernel (+ splitk_reduce_kernel)"
-    attn_desc += ", kv_append fused into it"
+    attn_desc += (", kv_append fused into it" if fused
+                  else ", kv_append as its own launch before it")
     res = {
         "metric": METRIC,
         "value": round(value, 2),

@@ -241,7 +241,10 @@ int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
  * paged_decode_step — one decode step: kv_append of every sequence's new
  * token, then paged_decode_attn_splitk_merged over the updated cache, with
  * the append done inside the attention kernel (one launch for groups of at
- * most 16 q heads; the reduce kernel follows for wider groups).
+ * most 16 q heads; the reduce kernel follows for wider groups). Above 1536
+ * (sequence, kv head) pairs the append is a launch of its own ahead of the
+ * attention, where that is faster; every argument is checked before either
+ * launch, so a rejected call writes nothing.
  *
  * Source: tiny-llm "优化", roadmap rows 分页 KV (the append is a scatter
  * through the block table) and FlashDecoding, and section 5 (the append
@@ -266,6 +269,12 @@ int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new,
                       const float* k_scale, const float* v_scale,
                       int32_t num_splits, void* workspace,
                       size_t workspace_bytes, void* out, hipStream_t stream);
+
+/* 1 when paged_decode_step with these dims appends inside the attention
+ * kernel, 0 when it issues the append as a launch of its own first (more
+ * than 1536 (sequence, kv head) pairs); a negative status for invalid dims.
+ * Lets a caller time or profile the attention launch on its own. */
+int32_t paged_decode_step_fuses_append(const pa_dims* dims);
 
 /* num_splits the library suggests for a batch whose longest context is
  * max_context_len tokens, assuming the batch's mean context is at least

@@ -22,7 +22,7 @@ __all__ = [
     "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
     "paged_decode_step",
     "splitk_workspace", "splitk_workspace_size",
-    "suggest_splits", "status_string", "version",
+    "suggest_splits", "step_fuses_append", "status_string", "version",
 ]
 
 KV_FP16 = 0
@@ -71,6 +71,7 @@ def load():
         "paged_decode_attn_splitk_merged": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
         "paged_decode_step": (I, [D, P, P, P, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
         "paged_decode_attn_suggest_splits": (I, [D, I]),
+        "paged_decode_step_fuses_append": (I, [D]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "pa_version": (I, []),
     }
@@ -290,3 +291,10 @@ def split_views(workspace, B, Hq, Hkv, S, D):
 
 def suggest_splits(d: PaDims, max_context_len: int) -> int:
     return int(load().paged_decode_attn_suggest_splits(ctypes.byref(d), int(max_context_len)))
+
+
+def step_fuses_append(d: PaDims) -> bool:
+    """Whether paged_decode_step appends inside the attention kernel for d."""
+    rc = int(load().paged_decode_step_fuses_append(ctypes.byref(d)))
+    _check("paged_decode_step_fuses_append", min(rc, 0))
+    return rc == 1

@@ -233,14 +233,22 @@ int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
 // merges inside the attention kernel.
 constexpr int kMergeInKernelMaxGroup = 16;
 
+// Most (sequence, kv head) pairs for which paged_decode_step appends inside
+// the attention kernel. Each worker owning a new token's tile writes it and
+// waits for the stores before its first tile load; with a pair for nearly
+// every worker that start-up wait on every worker costs more than one
+// separate append launch (measured on MI355X: fused ahead by 2-14 us up to
+// 1024 pairs, behind by 1-9 us at 2048).
+constexpr long long kFuseAppendMaxPairs = 1536;
+
 namespace {
 
-int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
-                const void* v_pages, const int32_t* block_table,
-                const int32_t* context_lens, float scale, const float* k_scale,
-                const float* v_scale, int32_t num_splits, void* workspace,
-                size_t workspace_bytes, void* out, hipStream_t stream,
-                const Fuse* fuse) {
+// Argument checks of the merged call, all done before anything is launched.
+int check_merged(const pa_dims* dims, const void* q, const void* k_pages,
+                 const void* v_pages, const int32_t* block_table,
+                 const int32_t* context_lens, const float* k_scale,
+                 const float* v_scale, int32_t num_splits, const void* workspace,
+                 size_t workspace_bytes, const void* out) {
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!q || !k_pages || !v_pages || !block_table || !context_lens || !out)
@@ -250,12 +258,26 @@ int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
   if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
   if ((long long)dims->num_seqs * dims->num_kv_heads * num_splits > INT_MAX)
     return PA_ERR_SHAPE;
+  if (dims->num_seqs > 0 && num_splits > 1 &&
+      (!workspace || workspace_bytes < ws_bytes(dims, num_splits)))
+    return PA_ERR_WORKSPACE;
+  return PA_OK;
+}
+
+int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
+                const void* v_pages, const int32_t* block_table,
+                const int32_t* context_lens, float scale, const float* k_scale,
+                const float* v_scale, int32_t num_splits, void* workspace,
+                size_t workspace_bytes, void* out, hipStream_t stream,
+                const Fuse* fuse) {
+  int rc = check_merged(dims, q, k_pages, v_pages, block_table, context_lens,
+                        k_scale, v_scale, num_splits, workspace,
+                        workspace_bytes, out);
+  if (rc) return rc;
   if (dims->num_seqs == 0) return PA_OK;
   if (num_splits == 1)   // one range per (sequence, kv head): the single pass
     return single_impl(dims, q, k_pages, v_pages, block_table, context_lens,
                        scale, k_scale, v_scale, out, stream, fuse);
-  if (!workspace || workspace_bytes < ws_bytes(dims, num_splits))
-    return PA_ERR_WORKSPACE;
   if (dims->num_q_heads / dims->num_kv_heads > kMergeInKernelMaxGroup) {
     // wide groups: one wave cannot merge G heads quickly; the reduce kernel
     // spreads the merge over a wave per (sequence, q head)
@@ -303,9 +325,23 @@ int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new,
                       const float* k_scale, const float* v_scale,
                       int32_t num_splits, void* workspace,
                       size_t workspace_bytes, void* out, hipStream_t stream) {
-  const int rc = check_dims(dims);
+  int rc = check_dims(dims);
   if (rc) return rc;
   if (!k_new || !v_new || !positions) return PA_ERR_NULL;
+  if (!paged_decode_step_fuses_append(dims)) {
+    // many pairs: the append as its own launch, then the merged call (the
+    // same bytes and the same output as the fused form)
+    rc = check_merged(dims, q, k_pages, v_pages, block_table, context_lens,
+                      k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                      out);
+    if (rc) return rc;
+    rc = kv_append(dims, dims->num_seqs, k_new, v_new, nullptr, positions,
+                   block_table, k_scale, v_scale, k_pages, v_pages, stream);
+    if (rc) return rc;
+    return merged_impl(dims, q, k_pages, v_pages, block_table, context_lens,
+                       scale, k_scale, v_scale, num_splits, workspace,
+                       workspace_bytes, out, stream, nullptr);
+  }
   const Fuse f{k_new, v_new, positions};
   return merged_impl(dims, q, k_pages, v_pages, block_table, context_lens,
                      scale, k_scale, v_scale, num_splits, workspace,
@@ -339,6 +375,12 @@ int paged_decode_attn_splitk_reduce(const pa_dims* dims,
   a.S = num_splits;
   a.cap = dims->max_blocks_per_seq * dims->block_size;
   return hip_status(pa::launch_reduce(a, dims->head_dim, stream));
+}
+
+int32_t paged_decode_step_fuses_append(const pa_dims* dims) {
+  const int rc = check_dims(dims);
+  if (rc) return rc;
+  return (long long)dims->num_seqs * dims->num_kv_heads <= kFuseAppendMaxPairs;
 }
 
 int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,

@@ -33,7 +33,8 @@ def test_header_declares_the_entry_points():
     for n in ["kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
               "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
               "paged_decode_step", "paged_decode_attn_splitk_workspace_size",
-              "paged_decode_attn_suggest_splits", "pa_status_string", "pa_version"]:
+              "paged_decode_attn_suggest_splits", "paged_decode_step_fuses_append",
+              "pa_status_string", "pa_version"]:
         assert n in names
 
 
@@ -101,6 +102,15 @@ def test_decode_step_validation():
     assert step(n=need - 1) == -5
     assert step(dims=good_dims(kv_dtype=pa.KV_FP8_E4M3FN)) == -3
     assert step(dims=good_dims(num_seqs=0)) == 0
+    # above 1536 (sequence, kv head) pairs the append is launched apart from
+    # the attention: every check still comes first, so nothing is launched
+    # (a launch on a machine without a GPU would report -6 instead)
+    big = good_dims(num_seqs=1000, num_kv_heads=2, num_q_heads=8)
+    need_big = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(big), 4)
+    assert step(dims=big, n=need_big - 1) == -5
+    assert step(dims=big, S=0) == -4
+    assert step(dims=big, out=None) == -1
+    assert step(dims=good_dims(num_seqs=1000, kv_dtype=pa.KV_FP8_E4M3FN)) == -3
 
 
 def test_fp8_requires_scales():
@@ -172,3 +182,16 @@ def test_suggest_splits():
     assert pa.suggest_splits(d4, 40) == 3           # two tiles -> at most 3
     d3 = pa.PaDims(64, 96, 1, 128, 32, 20000, 256, pa.KV_FP16)
     assert pa.suggest_splits(d3, 8192) == 64
+
+
+def test_decode_step_fusion_query():
+    """The step appends inside the attention kernel up to 1536 (sequence,
+    kv head) pairs and in a launch of its own above."""
+    assert pa.step_fuses_append(good_dims()) is True
+    assert pa.step_fuses_append(good_dims(num_seqs=768, num_kv_heads=2)) is True
+    assert pa.step_fuses_append(good_dims(num_seqs=769, num_kv_heads=2)) is False
+    assert pa.step_fuses_append(good_dims(num_seqs=256, num_kv_heads=8,
+                                          num_q_heads=64)) is False
+    assert pa.load().paged_decode_step_fuses_append(None) == -1
+    with pytest.raises(pa.PagedAttnError):
+        pa.step_fuses_append(good_dims(head_dim=96))

@@ -427,6 +427,47 @@ def test_fused_step_matches_append_then_merged(shape, kv_dtype):
     assert max_err(out, oracle_out(w)) <= TOL[kv_dtype]
 
 
+def _short_lens(n):
+    cycle = (0, 1, 3, 16, 31, 32, 33, 2, 7, 0, 20)
+    return tuple(cycle[i % len(cycle)] for i in range(n))
+
+
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("case", ["share-spans-many-pairs", "append-launched-apart"])
+def test_decode_step_many_pairs(case, kv_dtype):
+    """paged_decode_step with many short sequences (empty ones among them)
+    gives the bits of kv_append followed by the merged call.
+    share-spans-many-pairs: one long sequence and 300 short ones with two
+    splits, so each worker's share holds the long pair's 100 tiles or about
+    that many short pairs: the in-kernel append walks tens of pairs.
+    append-launched-apart: 2400 (sequence, kv head) pairs, above the count
+    where the step issues the append as a launch of its own."""
+    say("decode step, many pairs", case, kv_dtype)
+    pa = pa_mod()
+    if case == "share-spans-many-pairs":
+        lens, Hq, Hkv, S = (3200,) + _short_lens(300), 8, 2, 2
+    else:
+        lens, Hq, Hkv, S = _short_lens(300), 32, 8, 16
+    w = make_case(len(lens), Hq, Hkv, 128, 16, lens, kv_dtype=kv_dtype, seed=307)
+    a = DeviceWorkload(w, upto_last=True)
+    b = DeviceWorkload(w, upto_last=True)
+    ws_a = pa.splitk_workspace(a.q, a.k_pages, a.block_table, S)
+    ws_b = pa.splitk_workspace(b.q, b.k_pages, b.block_table, S)
+    pa.kv_append(a.new_k, a.new_v, a.k_pages, a.v_pages, a.block_table, a.positions,
+                 k_scale=a.k_scale, v_scale=a.v_scale)
+    ref = pa.paged_decode_attn_splitk_merged(a.q, a.k_pages, a.v_pages, a.block_table,
+                                             a.context_lens, a.scale, S, ws_a,
+                                             a.k_scale, a.v_scale)
+    out = pa.paged_decode_step(b.q, b.new_k, b.new_v, b.positions, b.k_pages, b.v_pages,
+                               b.block_table, b.context_lens, b.scale, S, ws_b,
+                               b.k_scale, b.v_scale)
+    torch.cuda.synchronize()
+    assert torch.equal(a.k_pages.view(torch.uint8), b.k_pages.view(torch.uint8))
+    assert torch.equal(a.v_pages.view(torch.uint8), b.v_pages.view(torch.uint8))
+    assert torch.equal(out, ref)
+    assert max_err(out, oracle_out(w)) <= TOL[kv_dtype]
+
+
 @pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
 @pytest.mark.parametrize("scale", [2.0, 4.0])
 def test_wide_score_range_exercises_the_rescale(scale, kv_dtype):

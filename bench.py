@@ -5,7 +5,9 @@ A step is the whole hot path over one batch: kv_append of every sequence's
 new token into its page, then decode attention over the sequence's context
 (the split pass with its log-sum-exp merge, or the single pass when the
 workload uses one split), issued as one paged_decode_step call: one kernel
-for groups of up to 16 q heads, the reduce kernel after it for wider ones. Inputs are seeded synthetic data already
+for groups of up to 16 q heads, the reduce kernel after it for wider ones;
+above 1536 (sequence, kv head) pairs the library launches the append apart,
+ahead of the attention. Inputs are seeded synthetic data already
 resident in HBM. R replicas of the KV pools rotate step to step so that the
 256 MB Infinity Cache cannot serve the working set. The R steps of one
 rotation (one per replica) are captured once as a HIP graph and replayed, as a
@@ -17,6 +19,10 @@ Prints ONE JSON line: metric / value (KV GB/s of the step) / unit, timing,
 average event-timed launch duration, against 8 TB/s) and `cpu_baseline`
 (the fp64 oracle timed on this host over a bounded sample of the same
 workload).
+
+The default 400 warm-up steps are there because the first milliseconds of
+replays after capture run up to 10% slow (seen on the wide MQA workload);
+the 1000 timed steps then take well under a second on every workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
   python bench.py --copy-only BYTES     # plain copy kernel for counter scaling
@@ -45,8 +51,8 @@ ATTN_LAUNCHES_PER_GRAPH = 8
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--splits", type=int, default=0, help="override the split count")
     ap.add_argument("--replicas", type=int, default=0, help="override pool replicas")
@@ -84,6 +90,17 @@ def measured_traffic(workload: str):
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def step_fuses_append(w) -> bool:
+    """Whether the library's decode step appends inside the attention kernel
+    for this workload (it issues the append apart for large pair counts)."""
+    import paged_mqa_gqa_amd as pa
+    cfg = w.cfg
+    d = pa.PaDims(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                  cfg.block_size, w.num_pages, cfg.max_blocks,
+                  pa.KV_FP16 if cfg.kv_dtype == "fp16" else pa.KV_FP8_E4M3FN)
+    return pa.step_fuses_append(d)
 
 
 def attention_algorithmic_bytes(w, with_append=True) -> int:
@@ -196,9 +213,7 @@ def main():
     group = cfg.num_q_heads // cfg.num_kv_heads
     # whether the library's step appends inside the attention kernel (it
     # issues the append as a launch of its own for large pair counts)
-    fused = (pa.step_fuses_append(pa.dims(cfg.num_seqs, cfg.num_q_heads, dw.k_pages,
-                                          dw.block_table))
-             and not args.separate_append)
+    fused = step_fuses_append(w) and not args.separate_append
 
     def attention(r):
         kp, vp = pools[r]

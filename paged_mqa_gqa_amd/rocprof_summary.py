@@ -55,7 +55,7 @@ def trace(args):
 
 
 def counters(args):
-    from bench import attention_algorithmic_bytes, kernel_source_hash
+    from bench import attention_algorithmic_bytes, kernel_source_hash, step_fuses_append
     from workloads import CONFIGS, Workload
     kib = 1024.0
     copy_prefix = "vectorized_elementwise_kernel"
@@ -70,7 +70,8 @@ def counters(args):
     fetch_b = statistics.median(af) * kib * f_fetch
     write_b = statistics.median(aw) * kib * f_write
     w = Workload(CONFIGS[args.workload])
-    alg = attention_algorithmic_bytes(w)
+    # the kernel's own bytes: the appended rows only when it does the append
+    alg = attention_algorithmic_bytes(w, with_append=step_fuses_append(w))
     lines = [
         f"# HBM traffic of {args.kernel} on workload {args.workload}",
         f"# command: {args.command}",

@@ -7,7 +7,10 @@
 //
 // One wave per (sequence, q head) row; each lane owns D/64 dimensions. The
 // split pass records how many partials each (sequence, kv head) received;
-// a sequence with no tokens gets zeros.
+// a sequence with no tokens gets zeros. The lane-parallel read of the lse
+// values and the output rows of up to kGroup partials in flight together
+// keep a row to a few memory round trips instead of two per partial; the
+// partials are still folded one after the other in index order.
 #include "launch.h"
 #include "device_common.h"
 
@@ -16,40 +19,66 @@ namespace pa {
 template <int D>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
   constexpr int kPer = D / 64;                // dims per lane (1 or 2)
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int kGroup = 16;                  // partial rows loaded together
+  const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   if (row >= a.B * a.Hq) return;
   const int b = row / a.Hq;
   const int h = (row % a.Hq) / a.G;
-  int L = a.context_lens[b];
+  int L = load_uniform(a.context_lens + b);
   L = L < 0 ? 0 : (L > a.cap ? a.cap : L);
   int n = 0;
   if (L > 0) {
-    n = a.ws_count[(long long)b * a.Hkv + h];
+    n = load_uniform(a.ws_count + (long long)b * a.Hkv + h);
     n = n < 1 ? 1 : (n > a.S ? a.S : n);
   }
   const float* lse = a.ws_lse + (long long)row * a.S;
-  const float* o = a.ws_o + (long long)row * a.S * D;
+  const float* o = a.ws_o + (long long)row * a.S * D + lane * kPer;
 
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, lse[i]);
+  // M = max_i lse_i, lanes over partials
+  const float l0 = lane < n ? lse[lane] : -INFINITY;
+  float M = l0;
+  for (int c = 64; c < n; c += 64) M = fmaxf(M, c + lane < n ? lse[c + lane] : -INFINITY);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, xor_lanes(M, m));
+
   float acc[kPer];
 #pragma unroll
   for (int k = 0; k < kPer; ++k) acc[k] = 0.0f;
   float den = 0.0f;
   if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
-      const float li = lse[i];
-      if (li == -INFINITY) continue;           // wave-uniform
-      const float w = __builtin_amdgcn_exp2f((li - M) * kLog2e);
-      den += w;
-      const float* oi = o + (long long)i * D + lane * kPer;
-      if constexpr (kPer == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(oi);
-        acc[0] += w * v.x;
-        acc[1] += w * v.y;
-      } else {
-        acc[0] += w * oi[0];
+    for (int c = 0; c < n; c += 64) {
+      // weight of partial c + lane; an empty partial (lse = -inf) weighs
+      // zero and its output row is never used
+      const float li = c == 0 ? l0 : (c + lane < n ? lse[c + lane] : -INFINITY);
+      const float wl = li == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((li - M) * kLog2e);
+      const int m = min(64, n - c);
+      for (int j0 = 0; j0 < m; j0 += kGroup) {
+        float v[kGroup][kPer];
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const float* oi = o + (long long)(c + min(j0 + j, m - 1)) * D;
+          if constexpr (kPer == 2) {
+            const float2 t = *reinterpret_cast<const float2*>(oi);
+            v[j][0] = t.x;
+            v[j][1] = t.y;
+          } else {
+            v[j][0] = oi[0];
+          }
+        }
+        // Branch-free fold, so that every load above stays in flight:
+        // slots past the chunk's last partial read lanes whose weight is
+        // zero, and a zero weight (empty partial) folds in an exact zero
+        // whatever its row holds.
+#pragma unroll
+        for (int j = 0; j < kGroup; ++j) {
+          const float w = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(wl), j0 + j));
+          den += w;
+#pragma unroll
+          for (int k = 0; k < kPer; ++k)
+            acc[k] = __builtin_fmaf(w, w != 0.0f ? v[j][k] : 0.0f, acc[k]);
+        }
       }
     }
   }

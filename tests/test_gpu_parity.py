@@ -279,14 +279,16 @@ def test_split_pass_partials_and_merge(S, kv_dtype):
     assert max_err(out, full) <= TOL[kv_dtype]
 
 
-@pytest.mark.parametrize("S", [1, 2, 5, 64])
-def test_reduce_kernel_matches_oracle_merge(S):
+@pytest.mark.parametrize("S,D", [(1, 64), (2, 64), (5, 64), (64, 64), (100, 64), (17, 128)])
+def test_reduce_kernel_matches_oracle_merge(S, D):
     """The merge kernel alone, on partials computed by the oracle (page-aligned
-    equal chunks), placed in the documented workspace layout."""
-    say("reduce", S)
+    equal chunks), placed in the documented workspace layout. Empty chunks
+    (lse = -inf) get NaN output rows, which must never reach the result;
+    S = 100 spans two 64-lane chunks of partials."""
+    say("reduce", S, D)
     pa = pa_mod()
     lens = (0, 1, 100, 777, 3000)
-    B, Hq, Hkv, D = len(lens), 12, 3, 64
+    B, Hq, Hkv = len(lens), 12, 3
     w = make_case(B, Hq, Hkv, D, 16, lens, seed=250 + S)
     k, v, _, _ = oracle_pools(w)
     o_r, lse_r = oracle.decode_partials(w.q, k, v, w.block_table, w.context_lens,
@@ -296,7 +298,10 @@ def test_reduce_kernel_matches_oracle_merge(S):
     nbytes = pa.splitk_workspace_size(d, S)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     o_v, lse_v, cnt_v = pa.split_views(ws, B, Hq, Hkv, S, D)
-    o_v.copy_(torch.from_numpy(o_r.astype(np.float32)))
+    o_poisoned = o_r.astype(np.float32)
+    o_poisoned[np.isneginf(lse_r)] = np.nan
+    assert np.isnan(o_poisoned).any()
+    o_v.copy_(torch.from_numpy(o_poisoned))
     lse_v.copy_(torch.from_numpy(lse_r.astype(np.float32)))
     cnt_v.fill_(S)
     lens_t = torch.tensor(lens, dtype=torch.int32, device="cuda")

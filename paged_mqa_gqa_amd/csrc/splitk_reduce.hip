@@ -25,18 +25,37 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
   if (row >= a.B * a.Hq) return;
   const int b = row / a.Hq;
   const int h = (row % a.Hq) / a.G;
-  int L = load_uniform(a.context_lens + b);
-  L = L < 0 ? 0 : (L > a.cap ? a.cap : L);
-  int n = 0;
-  if (L > 0) {
-    n = load_uniform(a.ws_count + (long long)b * a.Hkv + h);
-    n = n < 1 ? 1 : (n > a.S ? a.S : n);
-  }
   const float* lse = a.ws_lse + (long long)row * a.S;
   const float* o = a.ws_o + (long long)row * a.S * D + lane * kPer;
 
-  // M = max_i lse_i, lanes over partials
+  // The partial count and the context length first (scalar loads issued
+  // together); then the lse values and the output rows of the first kGroup
+  // partials, all in flight at once.
+  const int cnt = load_uniform(a.ws_count + (long long)b * a.Hkv + h);
+  const int L = load_uniform(a.context_lens + b);
+  const int n = (L <= 0 || a.cap <= 0) ? 0 : (cnt < 1 ? 1 : (cnt > a.S ? a.S : cnt));
+
+  // Output rows of partials first .. first + kGroup - 1; slots past the
+  // count repeat the last partial's row (no extra traffic, weight zero).
+  auto load_rows = [&](float (&v)[kGroup][kPer], int first) {
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const float* oi = o + (long long)min(first + j, max(n - 1, 0)) * D;
+      if constexpr (kPer == 2) {
+        const float2 t = *reinterpret_cast<const float2*>(oi);
+        v[j][0] = t.x;
+        v[j][1] = t.y;
+      } else {
+        v[j][0] = oi[0];
+      }
+    }
+  };
+
   const float l0 = lane < n ? lse[lane] : -INFINITY;
+  float v[kGroup][kPer];
+  load_rows(v, 0);
+
+  // M = max_i lse_i, lanes over partials
   float M = l0;
   for (int c = 64; c < n; c += 64) M = fmaxf(M, c + lane < n ? lse[c + lane] : -INFINITY);
 #pragma unroll
@@ -48,28 +67,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(ReduceArgs a) {
   float den = 0.0f;
   if (M != -INFINITY) {
     for (int c = 0; c < n; c += 64) {
-      // weight of partial c + lane; an empty partial (lse = -inf) weighs
-      // zero and its output row is never used
+      // weight of partial c + lane; an empty partial (lse = -inf) and a slot
+      // past the count weigh zero, and their output rows are never used
       const float li = c == 0 ? l0 : (c + lane < n ? lse[c + lane] : -INFINITY);
       const float wl = li == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f((li - M) * kLog2e);
       const int m = min(64, n - c);
       for (int j0 = 0; j0 < m; j0 += kGroup) {
-        float v[kGroup][kPer];
-#pragma unroll
-        for (int j = 0; j < kGroup; ++j) {
-          const float* oi = o + (long long)(c + min(j0 + j, m - 1)) * D;
-          if constexpr (kPer == 2) {
-            const float2 t = *reinterpret_cast<const float2*>(oi);
-            v[j][0] = t.x;
-            v[j][1] = t.y;
-          } else {
-            v[j][0] = oi[0];
-          }
-        }
-        // Branch-free fold, so that every load above stays in flight:
-        // slots past the chunk's last partial read lanes whose weight is
-        // zero, and a zero weight (empty partial) folds in an exact zero
-        // whatever its row holds.
+        if (c + j0 > 0) load_rows(v, c + j0);
+        // Branch-free fold in index order, so that every load above stays
+        // in flight: slots past the chunk's last partial read lanes whose
+        // weight is zero, and a zero weight folds in an exact zero whatever
+        // the row holds.
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) {
           const float w = __int_as_float(

@@ -314,6 +314,19 @@ def test_reduce_kernel_matches_oracle_merge(S, D):
     assert max_err(out, ref) <= 2e-3
 
 
+@pytest.mark.parametrize("Hq", [8, 32], ids=["merge-in-kernel", "reduce-kernel"])
+def test_max_splits_one_long_sequence(Hq):
+    """The largest split count (1024): one 40000-token sequence on one kv
+    head is 1250 tiles, so the 1024 workers cut it into 1024 partials. With
+    8 q heads the last worker to arrive merges all of them; with 32 the
+    reduce kernel does, over 16 chunks of 64 partials."""
+    say("max splits", Hq)
+    w = make_case(1, Hq, 1, 128, 16, (40000,), seed=308)
+    dw = DeviceWorkload(w)
+    err = max_err(gpu_decode(dw, 1024, merged=True), oracle_out(w))
+    assert err <= TOL["fp16"], err
+
+
 def test_output_bitwise_invariant_under_page_permutation():
     say("page permutation")
     lens = (300, 77, 1000)

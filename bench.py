@@ -133,7 +133,7 @@ def cpu_baseline(w, budget_s: float):
         threads = 1
     from workloads.device import remap_pages
     cfg = w.cfg
-    ks, vs = w.fp8_scales()
+    ks, vs = w.kv_scales()
     nk, nv, pos = w.new_tokens()
     seqs_done, kv_done, t_total = 0, 0, 0.0
     for b in range(cfg.num_seqs):

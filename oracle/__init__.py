@@ -8,6 +8,7 @@ this package imports nothing from them.
 
 Contents
   fp8        e4m3fn decode/encode from the OCP 8-bit floating point format
+  int8       symmetric int8 codes with a per-head scale
   paged      cache append (scatter) and block-table gather
   attention  single-token decode attention, split partials and their merge
 
@@ -25,8 +26,9 @@ Sources, by page title and section:
 
 Parity status: every function here is pinned by tests/test_oracle_*.py
 against closed forms, library routines (torch SDPA in float64, torch's
-float8_e4m3fn cast, scipy logsumexp), mpmath brute force and invariants.
+float8_e4m3fn cast, torch's round-half-even and clamp, scipy logsumexp),
+mpmath brute force and invariants.
 """
-from . import fp8, paged, attention  # noqa: F401
+from . import fp8, int8, paged, attention  # noqa: F401
 from .attention import decode, decode_partials, merge_partials, split_bounds  # noqa: F401
 from .paged import kv_append, gather, empty_pools  # noqa: F401

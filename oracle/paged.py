@@ -9,23 +9,27 @@ pages give no layout; the library's header fixes it and this file follows it.
 Pools are arrays [P, Hkv, bs, d] (the allocation shape); the bs * d
 elements of one (page, head) tile are stored in the order below, in units
 of 16-token blocks (blk = t // 16, r = t % 16; X = elements per 16 bytes:
-8 for fp16, 16 for fp8; rho(r) = r with its bits 2 and 3 swapped):
+8 for fp16, 16 for the one-byte codes; rho(r) = r with its bits 2 and 3 swapped):
 
   K element (t, i):  ((blk * (d / X) + i // X) * 16 + rho(r)) * X + i % X
   V element (t, i):  (((blk * (d / 16) + i // 16) * 2 + r // 8) * 16 + i % 16) * 8 + r % 8
 
 Token t of sequence b lives in page block_table[b, t // bs], slot t % bs.
-Element type is float16 or the uint8 code of fp8 e4m3fn; for fp8 each kv head
-h has its own float32 scale for K and for V (value = decode(code) * scale).
+Element type is float16, the uint8 code of fp8 e4m3fn, or an int8 code; for
+the one-byte types each kv head h has its own float32 scale for K and for V
+(value = decode(code) * scale).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from . import fp8
+from . import fp8, int8
+
+KV_DTYPES = ("fp16", "fp8_e4m3fn", "int8")
 
 
 def chunk_elems(kv_dtype) -> int:
+    """Elements per 16-byte chunk: 8 two-byte or 16 one-byte values."""
     return 8 if kv_dtype == "fp16" else 16
 
 
@@ -50,14 +54,22 @@ def v_offset(t, i, d):
 
 
 def empty_pools(num_pages, num_kv_heads, block_size, head_dim, kv_dtype):
-    """Pools filled with NaN (fp16 0x7E00, fp8 code 0x7F): never-written slots."""
+    """Pools whose every slot holds the never-written marker: NaN (fp16
+    0x7E00, fp8 code 0x7F) or the int8 code -128 that no append produces."""
     shape = (num_pages, num_kv_heads, block_size, head_dim)
     if kv_dtype == "fp16":
         return np.full(shape, np.nan, np.float16), np.full(shape, np.nan, np.float16)
     if kv_dtype == "fp8_e4m3fn":
         return (np.full(shape, fp8.NAN_CODE, np.uint8),
                 np.full(shape, fp8.NAN_CODE, np.uint8))
+    if kv_dtype == "int8":
+        return (np.full(shape, int8.POISON_CODE, np.int8),
+                np.full(shape, int8.POISON_CODE, np.int8))
     raise ValueError(kv_dtype)
+
+
+def _codec(kv_dtype):
+    return {"fp8_e4m3fn": fp8, "int8": int8}[kv_dtype]
 
 
 def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
@@ -65,8 +77,9 @@ def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
     """Write token i's K/V rows into (block_table[seq_ids[i], pos // bs], pos % bs).
 
     k_new, v_new: float16 [T, Hkv, d]; seq_ids, positions: int [T].
-    fp16 pools receive the bits unchanged; fp8 pools receive
-    fp8.quantize(x, scale[h]) per head. Returns new pools (inputs untouched).
+    fp16 pools receive the bits unchanged; fp8 / int8 pools receive
+    quantize(x, scale[h]) of that codec per head. Returns new pools (inputs
+    untouched).
     """
     P, H, bs, d = k_pages.shape
     X = chunk_elems(kv_dtype)
@@ -82,8 +95,8 @@ def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
     else:
         ks = np.asarray(k_scale, np.float32)[None, :, None]
         vs = np.asarray(v_scale, np.float32)[None, :, None]
-        kw = fp8.quantize(k_new, ks)
-        vw = fp8.quantize(v_new, vs)
+        kw = _codec(kv_dtype).quantize(k_new, ks)
+        vw = _codec(kv_dtype).quantize(v_new, vs)
     dims = np.arange(d)
     ko = k_offset(slot[:, None], dims[None, :], d, X)         # [T, d]
     vo = v_offset(slot[:, None], dims[None, :], d)
@@ -108,5 +121,6 @@ def gather(k_pages, v_pages, block_table, b, h, L, kv_dtype="fp16",
     v = vf[page[:, None], h, v_offset(slot[:, None], dims[None, :], d)]
     if kv_dtype == "fp16":
         return k.astype(np.float64), v.astype(np.float64)
-    return (fp8.decode(k) * np.float64(k_scale[h]),
-            fp8.decode(v) * np.float64(v_scale[h]))
+    c = _codec(kv_dtype)
+    return (c.decode(k) * np.float64(k_scale[h]),
+            c.decode(v) * np.float64(v_scale[h]))

@@ -17,7 +17,7 @@ def oracle_pools(w: Workload, seqs=None, upto_last=False):
     k, v = oracle.empty_pools(w.num_pages, cfg.num_kv_heads, cfg.block_size,
                               cfg.head_dim, cfg.kv_dtype)
     K, V, sid, pos = w.tokens(seqs, upto_last)
-    ks, vs = w.fp8_scales()
+    ks, vs = w.kv_scales()
     k, v = oracle.kv_append(k, v, w.block_table, sid, pos, K, V, cfg.kv_dtype,
                             ks, vs)
     return k, v, ks, vs

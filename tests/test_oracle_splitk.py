@@ -152,7 +152,7 @@ def test_layout_offsets_are_a_bijection_of_the_tile():
                           [[_tile_pos_v(a, b, 128) for b in range(128)] for a in range(64)])
 
 
-@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("kv_dtype", ["fp16", "fp8_e4m3fn", "int8"])
 def test_append_then_attend_equals_full_pool(kv_dtype):
     w, bk, bv, k2, v2, kn, vn, pos, ks, vs = _append_case(kv_dtype)
     fk, fv, _, _ = oracle_pools(w)
@@ -161,7 +161,7 @@ def test_append_then_attend_equals_full_pool(kv_dtype):
 
 def test_fp8_scales_bound_every_value():
     w = make_case(2, 4, 2, 32, 16, (40, 12), kv_dtype="fp8_e4m3fn", seed=26)
-    ks, vs = w.fp8_scales()
+    ks, vs = w.kv_scales()
     K, V, _, _ = w.tokens()
     yk = K.astype(np.float32) / ks[None, :, None]
     # amax / (amax/448) may land one float32 ulp above 448; anything below
@@ -169,3 +169,31 @@ def test_fp8_scales_bound_every_value():
     assert 447.0 <= np.abs(yk).max() < 464.0
     codes = fp8.quantize(K, ks[None, :, None])
     assert not np.any(codes == 0x7F) and not np.any(codes == 0xFF)
+
+
+def test_lse_of_matches_scipy_logsumexp_per_head():
+    """oracle.attention.lse_of: ln sum_t exp(scale q.k_t) over the whole
+    context of each (sequence, q head), on a group map where j // G and
+    j % Hkv disagree (G = 3, Hkv = 2), a scale far from 1, an fp8 cache and
+    an empty sequence (-inf). Scores are gathered by hand from the token
+    stream, not from the pools."""
+    for kv_dtype in ("fp16", "fp8_e4m3fn", "int8"):
+        w = make_case(3, 6, 2, 32, 16, (70, 0, 5), kv_dtype=kv_dtype, seed=31,
+                      scale=0.37)
+        k, v, ks, vs = oracle_pools(w)
+        got = oracle.attention.lse_of(w.q, k, v, w.block_table, w.context_lens,
+                                      w.scale, kv_dtype, ks, vs)
+        assert got.shape == (3, 6)
+        assert np.all(got[1] == -np.inf)
+        for b in (0, 2):
+            K, _ = w.token_kv(b)
+            for j in range(6):
+                h = j // 3
+                Kh = K[:, h, :].astype(np.float32)
+                if kv_dtype == "fp8_e4m3fn":
+                    Kh = fp8.decode(fp8.quantize(Kh, ks[h])) * np.float64(ks[h])
+                elif kv_dtype == "int8":
+                    from oracle import int8 as oi8
+                    Kh = oi8.quantize(Kh, ks[h]).astype(np.float64) * np.float64(ks[h])
+                s = 0.37 * (Kh.astype(np.float64) @ w.q[b, j].astype(np.float64))
+                assert abs(got[b, j] - scipy.special.logsumexp(s)) < 1e-12, (kv_dtype, b, j)

@@ -3,9 +3,10 @@
 This module is the only code that the oracle side and the GPU side of the
 tests and of the benchmark share. It draws random numbers, sequence lengths
 and the page assignment, and nothing else: it holds no attention arithmetic
-and no cache-append arithmetic. The one statistic computed here is the fp8
-calibration scale of each kv head (its absolute maximum divided by 448, the
-largest e4m3fn value), an input that both sides receive unchanged.
+and no cache-append arithmetic. The one statistic computed here is the
+calibration scale of each kv head of a one-byte cache (its absolute maximum
+divided by the largest code: 448 for fp8 e4m3fn, 127 for int8), an input that
+both sides receive unchanged.
 
 Shapes follow the workloads of the decode path being modelled:
   * the MHA/MQA definitions on "TensorRT对Multi-Query Attention的专项优化支持"
@@ -30,6 +31,9 @@ import math
 import numpy as np
 
 FP8_E4M3FN_MAX = 448.0
+INT8_MAX = 127.0
+# largest code magnitude of each one-byte cache type (the calibration divisor)
+CODE_MAX = {"fp8_e4m3fn": FP8_E4M3FN_MAX, "int8": INT8_MAX}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -40,7 +44,7 @@ class Config:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    kv_dtype: str          # "fp16" or "fp8_e4m3fn"
+    kv_dtype: str          # "fp16", "fp8_e4m3fn" or "int8"
     std: float             # standard deviation of q, K and V draws
     lens: tuple            # ("fixed", l0, l1, ...), ("uniform", lo, hi),
                            # ("const", L) or ("lognormal", median, sigma, lo, hi)
@@ -64,7 +68,7 @@ class Config:
 
     @property
     def kv_bytes_per_elem(self) -> int:
-        return 1 if self.kv_dtype == "fp8_e4m3fn" else 2
+        return 2 if self.kv_dtype == "fp16" else 1
 
 
 CONFIGS = {
@@ -91,9 +95,16 @@ CONFIGS = {
     "mixed_fp8": Config("mixed_fp8", 256, 64, 8, 128, 16, "fp8_e4m3fn", 1.0,
                         ("lognormal", 1024, 1.0, 1, 32768), 32768, 16,
                         seed=1005),
+    # The same mixed batch with an int8 cache (symmetric codes, per-kv-head
+    # K and V scales): the cache precision that must not share one scale
+    # between K and V.
+    "mixed_int8": Config("mixed_int8", 256, 64, 8, 128, 16, "int8", 1.0,
+                         ("lognormal", 1024, 1.0, 1, 32768), 32768, 16,
+                         seed=1005),
 }
 
-CONFIG_ORDER = ["tiny_mqa", "gqa_llama", "wide_mqa", "long_splitk", "mixed_fp8"]
+CONFIG_ORDER = ["tiny_mqa", "gqa_llama", "wide_mqa", "long_splitk", "mixed_fp8",
+                "mixed_int8"]
 
 
 def _stream(seed: int, tag: int, *extra: int) -> np.random.Generator:
@@ -212,9 +223,11 @@ class Workload:
                 k[b] = kb[-1]; v[b] = vb[-1]
         return k, v, (self.context_lens - 1).astype(np.int32)
 
-    # -- fp8 calibration --------------------------------------------------
-    def fp8_scales(self):
-        """Per-kv-head fp32 scales: amax over all of that head's values / 448.
+    # -- one-byte cache calibration ----------------------------------------
+    def kv_scales(self):
+        """Per-kv-head fp32 scales of a one-byte cache: amax over all of that
+        head's K (resp. V) values / the largest code (448 for fp8 e4m3fn,
+        127 for int8).
 
         Returns (k_scale, v_scale), float32 [Hkv]. fp16 workloads get ones.
         """
@@ -222,7 +235,8 @@ class Workload:
         if self._scales is None:
             H = cfg.num_kv_heads
             ka = np.zeros(H, np.float32); va = np.zeros(H, np.float32)
-            if cfg.kv_dtype == "fp8_e4m3fn":
+            if cfg.kv_dtype in CODE_MAX:
+                qmax = np.float32(CODE_MAX[cfg.kv_dtype])
                 for b in range(cfg.num_seqs):
                     k, v = self.token_kv(b)
                     if k.shape[0] == 0:
@@ -230,8 +244,8 @@ class Workload:
                     ka = np.maximum(ka, np.abs(k).max(axis=(0, 2)).astype(np.float32))
                     va = np.maximum(va, np.abs(v).max(axis=(0, 2)).astype(np.float32))
                 # a head with no data at all keeps scale 1
-                ks = np.where(ka > 0, ka / np.float32(FP8_E4M3FN_MAX), np.float32(1))
-                vs = np.where(va > 0, va / np.float32(FP8_E4M3FN_MAX), np.float32(1))
+                ks = np.where(ka > 0, ka / qmax, np.float32(1))
+                vs = np.where(va > 0, va / qmax, np.float32(1))
             else:
                 ks = np.ones(H, np.float32); vs = np.ones(H, np.float32)
             self._scales = (ks.astype(np.float32), vs.astype(np.float32))

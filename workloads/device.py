@@ -1,6 +1,7 @@
 """Device copies of a seeded workload for the GPU library (tests, benchmark).
 
-The pools start as NaN (fp16 0x7E00 / fp8 code 0x7F) and are filled by the
+The pools start as never-written markers (fp16 NaN 0x7E00, fp8 NaN code 0x7F,
+int8 code -128, which no append produces) and are filled by the
 library's own kv_append, one call per group of sequences, with the tokens the
 generator draws; nothing here computes any part of attention or of the cache
 append. Pass `upto_last=True` to leave each sequence's final token out of the
@@ -20,6 +21,9 @@ def _nan_pools(w: Workload, device):
     if cfg.kv_dtype == "fp16":
         k = torch.full(shape_k, float("nan"), dtype=torch.float16, device=device)
         v = torch.full(shape_v, float("nan"), dtype=torch.float16, device=device)
+    elif cfg.kv_dtype == "int8":
+        k = torch.full(shape_k, -128, dtype=torch.int8, device=device)
+        v = torch.full(shape_v, -128, dtype=torch.int8, device=device)
     else:
         k = torch.full(shape_k, 0x7F, dtype=torch.uint8, device=device)
         v = torch.full(shape_v, 0x7F, dtype=torch.uint8, device=device)
@@ -45,7 +49,7 @@ class DeviceWorkload:
         self.q = torch.from_numpy(w.q).to(device)
         self.block_table = torch.from_numpy(w.block_table).to(device)
         self.context_lens = torch.from_numpy(w.context_lens).to(device)
-        ks, vs = w.fp8_scales()
+        ks, vs = w.kv_scales()
         if cfg.kv_dtype == "fp16":
             self.k_scale = self.v_scale = None
         else:

@@ -102,6 +102,26 @@ def decode_partials(q, k_pages, v_pages, block_table, context_lens, scale,
     return o, lse
 
 
+def range_partial(q, k_pages, v_pages, block_table, b, h, start, end, scale,
+                  kv_dtype="fp16", k_scale=None, v_scale=None):
+    """Attention of the G q heads of kv group h of sequence b over the tokens
+    [start, end) alone: their normalised output o [G, d] and
+    lse [G] = ln sum_{start <= t < end} exp(s_t) (natural log); an empty
+    range gives o = 0 and lse = -inf."""
+    q = np.asarray(q).astype(np.float64)
+    Hq, d = q.shape[1], q.shape[2]
+    Hkv = k_pages.shape[1]
+    G = Hq // Hkv
+    if end <= start:
+        return np.zeros((G, d)), np.full(G, -math.inf)
+    k, v = gather(k_pages, v_pages, block_table, b, h, end, kv_dtype, k_scale, v_scale)
+    s = _group_scores(q[b, h * G:(h + 1) * G], k[start:end], scale)       # [G, n]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ v[start:end]) / l, (m + np.log(l))[:, 0]
+
+
 def merge_partials(o, lse):
     """Log-sum-exp merge of split partials: [..., S, d], [..., S] -> [..., d]."""
     o = np.asarray(o, np.float64)

@@ -24,8 +24,9 @@ MAX = 448.0
 NAN_CODE = 0x7F
 
 
-def decode(codes) -> np.ndarray:
-    """Value of each e4m3fn code as float64 (NaN for 0x7F / 0xFF)."""
+def decode_closed_form(codes) -> np.ndarray:
+    """Value of each e4m3fn code as float64 (NaN for 0x7F / 0xFF), from the
+    format's definition."""
     c = np.asarray(codes).astype(np.int64) & 0xFF
     s = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 0xF
@@ -36,9 +37,19 @@ def decode(codes) -> np.ndarray:
     return np.where((e == 15) & ((c & 7) == 7), np.nan, val)
 
 
+# The value of every code, from the definition: decode() looks codes up here.
+DECODE_TABLE = decode_closed_form(np.arange(256))
+
+
+def decode(codes) -> np.ndarray:
+    """Value of each e4m3fn code as float64 (NaN for 0x7F / 0xFF): the
+    definition above, evaluated once per code and looked up."""
+    return DECODE_TABLE[np.asarray(codes).astype(np.uint8)]
+
+
 # All non-negative finite codes 0x00..0x7E in increasing value order.
 _POS_CODES = np.arange(0x7F, dtype=np.int64)
-_POS_VALS = decode(_POS_CODES)
+_POS_VALS = decode_closed_form(_POS_CODES)
 assert np.all(np.diff(_POS_VALS) > 0)
 
 
@@ -60,7 +71,7 @@ def encode(y) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def quantize(x_fp16, scale_fp32) -> np.ndarray:
+def quantize_direct(x_fp16, scale_fp32) -> np.ndarray:
     """Cache-append rule for fp8: encode(float32(x) / float32(scale)).
 
     The division is one IEEE float32 division (round to nearest even), the
@@ -72,3 +83,24 @@ def quantize(x_fp16, scale_fp32) -> np.ndarray:
     with np.errstate(divide="ignore", invalid="ignore"):
         y = x32 / np.asarray(scale_fp32, dtype=np.float32)
     return encode(y.astype(np.float32))
+
+
+ALL_FP16 = np.arange(65536, dtype=np.uint16).view(np.float16)
+
+
+def quantize(x_fp16, scale_fp32) -> np.ndarray:
+    """quantize_direct for fp16 input, evaluated per scale value as a table
+    over all 65536 fp16 inputs (the same arithmetic on the same operands)
+    and looked up by each element's bit pattern."""
+    x = np.asarray(x_fp16, dtype=np.float16)
+    scale = np.asarray(scale_fp32, dtype=np.float32)
+    if np.isnan(scale).any():
+        return quantize_direct(x, scale)
+    shape = np.broadcast_shapes(x.shape, scale.shape)
+    bits = np.broadcast_to(x.view(np.uint16), shape)
+    out = np.empty(shape, np.uint8)
+    for u in np.unique(scale):
+        table = quantize_direct(ALL_FP16, u)
+        sel = np.broadcast_to(scale == u, shape)
+        out[sel] = table[bits[sel]]
+    return out

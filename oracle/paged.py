@@ -73,18 +73,24 @@ def _codec(kv_dtype):
 
 
 def kv_append(k_pages, v_pages, block_table, seq_ids, positions, k_new, v_new,
-              kv_dtype="fp16", k_scale=None, v_scale=None):
+              kv_dtype="fp16", k_scale=None, v_scale=None, inplace=False):
     """Write token i's K/V rows into (block_table[seq_ids[i], pos // bs], pos % bs).
 
     k_new, v_new: float16 [T, Hkv, d]; seq_ids, positions: int [T].
     fp16 pools receive the bits unchanged; fp8 / int8 pools receive
     quantize(x, scale[h]) of that codec per head. Returns new pools (inputs
-    untouched).
+    untouched), or with inplace=True writes into the given pools (which must
+    be contiguous) and returns them.
     """
     P, H, bs, d = k_pages.shape
     X = chunk_elems(kv_dtype)
-    kf = k_pages.copy().reshape(P, H, bs * d)
-    vf = v_pages.copy().reshape(P, H, bs * d)
+    if inplace:
+        assert k_pages.flags.c_contiguous and v_pages.flags.c_contiguous
+        kf = k_pages.reshape(P, H, bs * d)
+        vf = v_pages.reshape(P, H, bs * d)
+    else:
+        kf = k_pages.copy().reshape(P, H, bs * d)
+        vf = v_pages.copy().reshape(P, H, bs * d)
     seq_ids = np.asarray(seq_ids, np.int64)
     positions = np.asarray(positions, np.int64)
     page = np.asarray(block_table, np.int64)[seq_ids, positions // bs]

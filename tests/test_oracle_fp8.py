@@ -113,3 +113,15 @@ def test_roundtrip_every_finite_code():
     v = fp8.decode(codes)
     fin = ~np.isnan(v)
     assert np.array_equal(fp8.encode(v[fin].astype(np.float32)), codes[fin])
+
+
+def test_tabulated_quantize_and_decode_equal_the_direct_rules():
+    """quantize() (a table over all fp16 inputs per scale) and decode() (a
+    table over the 256 codes) give the bits of the direct definitions."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((50, 4, 64)) * 3).astype(np.float16)
+    x[0, 0, :4] = [np.inf, -np.inf, np.nan, 0.0]
+    for s in (np.float32(0.0123), np.array([0.01, 0.5, 2.0, 0.01], np.float32)[None, :, None]):
+        assert np.array_equal(fp8.quantize(x, s), fp8.quantize_direct(x, s))
+    c = rng.integers(0, 256, 5000)
+    assert np.array_equal(fp8.decode(c), fp8.decode_closed_form(c), equal_nan=True)

@@ -197,3 +197,43 @@ def test_lse_of_matches_scipy_logsumexp_per_head():
                     Kh = oi8.quantize(Kh, ks[h]).astype(np.float64) * np.float64(ks[h])
                 s = 0.37 * (Kh.astype(np.float64) @ w.q[b, j].astype(np.float64))
                 assert abs(got[b, j] - scipy.special.logsumexp(s)) < 1e-12, (kv_dtype, b, j)
+
+
+def test_range_partial_matches_scipy_and_whole_context():
+    """oracle.attention.range_partial over [a, e): scipy softmax-weighted V
+    and logsumexp of hand-gathered scores; over [0, L) it is decode and
+    lse_of; adjacent ranges merge to their union."""
+    w = make_case(2, 6, 2, 32, 16, (150, 40), seed=32, scale=0.3)
+    k, v, ks, vs = oracle_pools(w)
+    full = oracle.decode(w.q, k, v, w.block_table, w.context_lens, w.scale)
+    tot = oracle.attention.lse_of(w.q, k, v, w.block_table, w.context_lens, w.scale)
+    K, V = w.token_kv(0)
+    for h in range(2):
+        for a, e in ((0, 32), (32, 150), (17, 18), (64, 64), (0, 150)):
+            o, lse = oracle.attention.range_partial(w.q, k, v, w.block_table, 0, h, a, e,
+                                                    w.scale)
+            for g in range(3):
+                j = h * 3 + g
+                if e <= a:
+                    assert lse[g] == -np.inf and np.all(o[g] == 0)
+                    continue
+                s = 0.3 * (K[a:e, h].astype(np.float64) @ w.q[0, j].astype(np.float64))
+                p = scipy.special.softmax(s)
+                assert np.max(np.abs(o[g] - p @ V[a:e, h].astype(np.float64))) < 1e-14
+                assert abs(lse[g] - scipy.special.logsumexp(s)) < 1e-12
+                if (a, e) == (0, 150):
+                    assert np.max(np.abs(o[g] - full[0, j])) < 1e-14
+                    assert abs(lse[g] - tot[0, j]) < 1e-12
+        o1, l1 = oracle.attention.range_partial(w.q, k, v, w.block_table, 0, h, 0, 64, w.scale)
+        o2, l2 = oracle.attention.range_partial(w.q, k, v, w.block_table, 0, h, 64, 150, w.scale)
+        m = oracle.merge_partials(np.stack([o1, o2], 1), np.stack([l1, l2], 1))
+        assert np.max(np.abs(m - full[0, h * 3:(h + 1) * 3])) < 1e-14
+
+
+def test_inplace_append_equals_copying_append():
+    w, bk, bv, k2, v2, kn, vn, pos, ks, vs = _append_case("fp8_e4m3fn")
+    ik, iv = bk.copy(), bv.copy()
+    rk, rv = oracle.kv_append(ik, iv, w.block_table, np.arange(3), pos, kn, vn,
+                              "fp8_e4m3fn", ks, vs, inplace=True)
+    assert np.shares_memory(rk, ik) and np.shares_memory(rv, iv)
+    assert np.array_equal(ik, k2) and np.array_equal(iv, v2)

@@ -147,10 +147,13 @@ class Workload:
     logical (position) order.
     """
 
-    def __init__(self, cfg: Config, seed: int | None = None):
+    def __init__(self, cfg: Config, seed: int | None = None, cache_tokens: bool = False):
         if seed is not None:
             cfg = dataclasses.replace(cfg, seed=seed)
         self.cfg = cfg
+        # keep each sequence's drawn K/V (same values, drawn once) for callers
+        # that read them several times over (full-size parity checks)
+        self._token_cache = {} if cache_tokens else None
         B, bs = cfg.num_seqs, cfg.block_size
         self.context_lens = draw_lengths(cfg)
         nblk = -(-self.context_lens.astype(np.int64) // bs)
@@ -181,6 +184,8 @@ class Workload:
 
     # -- token data -------------------------------------------------------
     def token_kv(self, b: int):
+        if self._token_cache is not None and b in self._token_cache:
+            return self._token_cache[b]
         cfg = self.cfg
         L = int(self.context_lens[b])
         rng = _stream(cfg.seed, 7, b)
@@ -189,6 +194,8 @@ class Workload:
              ).astype(np.float16)
         v = (rng.standard_normal(shape, dtype=np.float32) * cfg.std
              ).astype(np.float16)
+        if self._token_cache is not None:
+            self._token_cache[b] = (k, v)
         return k, v
 
     def tokens(self, seqs=None, upto_last: bool = False):
@@ -222,6 +229,21 @@ class Workload:
             if kb.shape[0]:
                 k[b] = kb[-1]; v[b] = vb[-1]
         return k, v, (self.context_lens - 1).astype(np.int32)
+
+    def step_inputs(self, step: int):
+        """q [B, Hq, d] and the new K / V rows [B, Hkv, d] (fp16) of decode
+        step `step` >= 1 after the one this draw describes, from streams of
+        their own (seed, 8, step): inputs for runs of several decode steps."""
+        cfg = self.cfg
+        rng = _stream(cfg.seed, 8, step)
+        B = cfg.num_seqs
+        q = (rng.standard_normal((B, cfg.num_q_heads, cfg.head_dim), dtype=np.float32)
+             * cfg.std).astype(np.float16)
+        k = (rng.standard_normal((B, cfg.num_kv_heads, cfg.head_dim), dtype=np.float32)
+             * cfg.std).astype(np.float16)
+        v = (rng.standard_normal((B, cfg.num_kv_heads, cfg.head_dim), dtype=np.float32)
+             * cfg.std).astype(np.float16)
+        return q, k, v
 
     # -- one-byte cache calibration ----------------------------------------
     def kv_scales(self):
@@ -259,8 +281,25 @@ class Workload:
             cfg.num_kv_heads * cfg.head_dim * 2 * cfg.kv_bytes_per_elem
 
 
-def make(name: str, seed: int | None = None) -> Workload:
-    return Workload(CONFIGS[name], seed)
+def arrivals(cfg: Config, count: int, tag: int):
+    """Prompts of `count` sequences joining a running batch: lengths from the
+    configuration's length recipe and K / V [L, Hkv, d] fp16 per prompt, from
+    streams keyed (seed, 10, tag) and (seed, 11, tag, i)."""
+    sub = dataclasses.replace(cfg, num_seqs=count, seed=cfg.seed)
+    lens = draw_lengths(dataclasses.replace(sub, seed=int(_stream(cfg.seed, 10, tag)
+                                                           .integers(2 ** 31))))
+    prompts = []
+    for i, L in enumerate(lens):
+        rng = _stream(cfg.seed, 11, tag, i)
+        shape = (int(L), cfg.num_kv_heads, cfg.head_dim)
+        k = (rng.standard_normal(shape, dtype=np.float32) * cfg.std).astype(np.float16)
+        v = (rng.standard_normal(shape, dtype=np.float32) * cfg.std).astype(np.float16)
+        prompts.append((k, v))
+    return lens, prompts
+
+
+def make(name: str, seed: int | None = None, cache_tokens: bool = False) -> Workload:
+    return Workload(CONFIGS[name], seed, cache_tokens)
 
 
 def make_case(num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,

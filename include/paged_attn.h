@@ -19,8 +19,8 @@
  *     read) and row FlashDecoding (long-context decode attention).
  *   - same tiny-llm page, section 2: the per-sequence KV size
  *     2 x layers x kv_heads x head_dim x max_seq_len x bytes.
- * The pages fix no memory layout, head-to-group map, split rule or fp8
- * format; the choices below are this library's.
+ * The pages fix no memory layout, head-to-group map, split rule or
+ * one-byte code format; the choices below are this library's.
  *
  * Conventions for every entry point
  *   - Tensor arguments are DEVICE pointers owned by the caller; `dims` is a
@@ -46,24 +46,27 @@
  *                                         (page, kv head), in the order below
  *   block_table     [B, max_blocks_per_seq] int32 page ids
  *   context_lens    [B]                   int32 tokens per sequence
- *   k_scale,v_scale [Hkv]                 fp32, fp8 caches only (else NULL)
+ *   k_scale,v_scale [Hkv]                 fp32, one-byte caches only (else NULL)
  * Inside a tile, slot t (0 <= t < bs) and dimension i (0 <= i < d) sit at
  * element offset, with blk = t / 16, r = t % 16, rho(r) = r with its bits
- * 2 and 3 swapped, and X = 16 bytes / element size (8 for fp16, 16 for fp8):
+ * 2 and 3 swapped, and X = 16 bytes / element size (8 for fp16, 16 for the
+ * one-byte codes):
  *   K:  ((blk * (d / X) + i / X) * 16 + rho(r)) * X + i % X
  *   V:  (((blk * (d / 16) + i / 16) * 2 + r / 8) * 16 + i % 16) * 8 + r % 8
  * i.e. each 16-token block stores K as 16-byte chunks of one token's row,
  * chunk-major, with slots 0-3, 8-11 in the first 8 rows and 4-7, 12-15 in
  * the last 8; and V as runs of 8 tokens of one dimension. This is the order
  * in which the kernels' matrix-core operands are loaded: a lane's V operand
- * is one 16-byte (fp16) or 8-byte (fp8) run and every wave-wide load reads
- * whole 128-byte lines. A page pool may be allocated as
+ * is one 16-byte (fp16) or 8-byte (one-byte codes) run and every wave-wide
+ * load reads whole 128-byte lines. A page pool may be allocated as
  * [P, Hkv, bs, d] (the binding does), but its last two axes are storage, not
  * a [token, dim] matrix. Caches are written through kv_append.
- * fp8 caches hold OCP E4M3FN codes (1 byte, max 448, no infinities); the
- * value of a code is decode(code) * scale[h]. Device buffers must be
- * 16-byte aligned (q, k_pages, v_pages, out, workspace) or 4-byte aligned
- * (k_new, v_new, index arrays, scales).
+ * fp8 caches hold OCP E4M3FN codes (1 byte, max 448, no infinities); int8
+ * caches hold symmetric codes in [-127, 127] (two's complement bytes; -128
+ * is never written); in both the value of a code is decode(code) *
+ * scale[h], with one scale per kv head for K and another for V. Device
+ * buffers must be 16-byte aligned (q, k_pages, v_pages, out, workspace) or
+ * 4-byte aligned (k_new, v_new, index arrays, scales).
  */
 #ifndef PAGED_ATTN_H
 #define PAGED_ATTN_H
@@ -79,19 +82,23 @@ extern "C" {
 enum pa_kv_dtype {
   PA_KV_FP16 = 0,        /* IEEE binary16 */
   PA_KV_FP8_E4M3FN = 1,  /* OCP E4M3FN code + per-kv-head fp32 scale */
+  PA_KV_INT8 = 2,        /* symmetric int8 code + per-kv-head fp32 scale */
 };
 
 enum pa_status {
   PA_OK = 0,
   PA_ERR_NULL = -1,       /* a required pointer is NULL */
   PA_ERR_SHAPE = -2,      /* unsupported or inconsistent sizes */
-  PA_ERR_DTYPE = -3,      /* unknown kv_dtype, or scales missing for fp8 */
+  PA_ERR_DTYPE = -3,      /* unknown kv_dtype, or scales missing for a
+                             one-byte cache */
   PA_ERR_SPLITS = -4,     /* num_splits outside [1, PA_MAX_SPLITS] */
   PA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required */
   PA_ERR_HIP = -6,        /* the kernel launch failed */
 };
 
 #define PA_MAX_SPLITS 1024
+/* Arrival counters at the start of every split workspace (see below). */
+#define PA_WORKSPACE_SEM_SLOTS 2048
 
 /* Sizes shared by every call on one cache. num_seqs may be 0 (no work). */
 typedef struct pa_dims {
@@ -122,6 +129,8 @@ typedef struct pa_dims {
  *   fp16 cache   : the fp16 bits are copied unchanged
  *   fp8 cache    : code = RNE_e4m3fn(float(x) / k_scale[h]) (IEEE fp32
  *                  division; magnitudes >= 448 saturate to +-448, NaN -> 0x7F)
+ *   int8 cache   : code = clamp(round_half_even(float(x) / k_scale[h]),
+ *                  -127, 127) (IEEE fp32 division; NaN -> 0)
  * Only the addressed slots are written. Two tokens addressing one slot is
  * undefined. positions[i] must be < max_blocks_per_seq * bs (out-of-range
  * positions or sequence ids are skipped).
@@ -143,7 +152,7 @@ int kv_append(const pa_dims* dims, int32_t num_tokens,
  * One workgroup per (sequence, kv head) covers that sequence's whole
  * context; `out` [B, Hq, d] fp16 receives the normalised result, rounded
  * to nearest even. Sequences with L = 0 get zeros. `scale` multiplies
- * q . k (typically 1/sqrt(d)). k_scale / v_scale: fp8 caches only.
+ * q . k (typically 1/sqrt(d)). k_scale / v_scale: one-byte caches only.
  */
 int paged_decode_attn(const pa_dims* dims, const void* q,
                       const void* k_pages, const void* v_pages,
@@ -155,12 +164,16 @@ int paged_decode_attn(const pa_dims* dims, const void* q,
  * Workspace bytes needed by paged_decode_attn_splitk and
  * paged_decode_attn_splitk_merged for num_splits partial slots per
  * (sequence, q head). Layout, densely packed in this order:
+ *   sem   int32   [PA_WORKSPACE_SEM_SLOTS]  arrival counters of the merged
+ *                                 call, at the same place for every dims and
+ *                                 num_splits: zero before the workspace's
+ *                                 first use (zero-fill it once); every
+ *                                 completed merged call leaves them zero, so
+ *                                 one workspace serves calls of any size in
+ *                                 turn (each within its own size)
  *   o     float32 [B, Hq, S, d]   normalised partial outputs
  *   lse   float32 [B, Hq, S]      natural-log sum of exp(scores) per partial
  *   count int32   [B, Hkv]        partials written for (sequence, kv head)
- *   sem   int32   [B, Hkv]        arrival counters of the merged call: must
- *                                 be zero before its first use; every
- *                                 completed merged call leaves them zero
  * Returns 0 for invalid dims or num_splits.
  */
 size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
@@ -269,6 +282,29 @@ int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new,
                       const float* k_scale, const float* v_scale,
                       int32_t num_splits, void* workspace,
                       size_t workspace_bytes, void* out, hipStream_t stream);
+
+/*
+ * paged_decode_advance — move a batch on by one decode step, on the device.
+ *
+ * Source: tiny-llm "优化", section 5 (the decode sequence is captured as a
+ * graph; the values that change from step to step, such as the visible
+ * length and the append position, are device ints in fixed buffers, so the
+ * same graph replays every step).
+ *
+ * For every sequence b with positions[b] >= 0 (a live slot): positions[b]
+ * += 1 and context_lens[b] += 1, so that paged_decode_step called again
+ * with the next token's q, k_new and v_new appends it after the previous
+ * one and attends over one more token. A slot whose next position would be
+ * at or past max_blocks_per_seq * block_size gets positions[b] = -1 (no
+ * further appends) and keeps its length. Slots with positions[b] < 0 are
+ * left alone. Captured after paged_decode_step in one graph, a replay is
+ * one whole decode step. The pages the next positions fall in must already
+ * be in the block table (a caller reserving ahead, such as the page manager
+ * below, writes them before the replays).
+ *   context_lens, positions: int32 [B], device, read and written.
+ */
+int paged_decode_advance(const pa_dims* dims, int32_t* context_lens,
+                         int32_t* positions, hipStream_t stream);
 
 /* 1 when paged_decode_step with these dims appends inside the attention
  * kernel, 0 when it issues the append as a launch of its own first (more

@@ -17,16 +17,22 @@ import os
 import torch
 
 __all__ = [
-    "PaDims", "PagedAttnError", "KV_FP16", "KV_FP8_E4M3FN", "library_path",
+    "PaDims", "PagedAttnError", "KV_FP16", "KV_FP8_E4M3FN", "KV_INT8", "library_path",
     "load", "dims", "kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
     "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
     "paged_decode_step",
+    "paged_decode_advance",
     "splitk_workspace", "splitk_workspace_size",
     "suggest_splits", "step_fuses_append", "status_string", "version",
+    "KvPageManager", "kv_bytes_per_sequence", "kv_pool_bytes", "kv_pages_for_budget",
 ]
 
 KV_FP16 = 0
 KV_FP8_E4M3FN = 1
+KV_INT8 = 2
+# int32 arrival counters at the start of every split workspace
+# (PA_WORKSPACE_SEM_SLOTS in include/paged_attn.h)
+WORKSPACE_SEM_SLOTS = 2048
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -70,9 +76,28 @@ def load():
         "paged_decode_attn_splitk_reduce": (I, [D, P, I, P, Z, P, P]),
         "paged_decode_attn_splitk_merged": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
         "paged_decode_step": (I, [D, P, P, P, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
+        "paged_decode_advance": (I, [D, P, P, P]),
         "paged_decode_attn_suggest_splits": (I, [D, I]),
         "paged_decode_step_fuses_append": (I, [D]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        # page manager (include/paged_kv_manager.h)
+        "pa_kv_elem_bytes": (I, [I]),
+        "pa_kv_bytes_per_sequence": (ctypes.c_int64, [I, I, I, I, I]),
+        "pa_kv_pool_bytes": (ctypes.c_int64, [I, I, I, I, I]),
+        "pa_kv_pages_for_budget": (ctypes.c_int64, [ctypes.c_int64, I, I, I, I, I]),
+        "pa_kvm_create": (P, [I, I, I, I]),
+        "pa_kvm_destroy": (None, [P]),
+        "pa_kvm_free_pages": (I, [P]),
+        "pa_kvm_live_slots": (I, [P]),
+        "pa_kvm_length": (I, [P, I]),
+        "pa_kvm_pages_held": (I, [P, I]),
+        "pa_kvm_admit": (I, [P, I]),
+        "pa_kvm_release": (I, [P, I]),
+        "pa_kvm_reserve_ahead": (I, [P, I]),
+        "pa_kvm_plan_step": (I, [P, P, P, P]),
+        "pa_kvm_commit_steps": (I, [P, I]),
+        "pa_kvm_block_table": (I, [P, P]),
+        "pa_kvm_batch_state": (I, [P, P, P]),
         "pa_version": (I, []),
     }
     for name, (res, args) in sig.items():
@@ -101,24 +126,55 @@ def _stream(stream):
 
 
 def _kv_dtype(pages: torch.Tensor) -> int:
+    """Cache kind from the pool's element type: float16 values, uint8 /
+    float8_e4m3fn for fp8 e4m3fn codes, int8 for symmetric int8 codes."""
     if pages.dtype == torch.float16:
         return KV_FP16
     if pages.dtype in (torch.uint8, torch.float8_e4m3fn):
         return KV_FP8_E4M3FN
+    if pages.dtype == torch.int8:
+        return KV_INT8
     raise TypeError(f"unsupported page dtype {pages.dtype}")
 
 
-def _need(t, name, dtype=None, ndim=None, cuda=True):
+def _need(t, name, dtype=None, ndim=None, shape=None):
+    """Check one tensor argument before its pointer crosses the ABI: present,
+    contiguous, of the given dtype, rank and exact shape. A mismatch raises
+    here, never inside a kernel. (Devices are checked by _on_gpu once every
+    shape is known to be right.)"""
     if t is None:
         raise ValueError(f"{name} is required")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if cuda and t.device.type != "cuda":
-        raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, has {t.dim()}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _on_gpu(**tensors):
+    """Every given tensor (None entries skipped) on the same GPU."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor, is on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _scales(d, k_scale, v_scale):
+    """Per-kv-head fp32 scales: required for one-byte caches, else ignored."""
+    if d.kv_dtype == KV_FP16:
+        return None, None
+    _need(k_scale, "k_scale", torch.float32, 1, shape=(d.num_kv_heads,))
+    _need(v_scale, "v_scale", torch.float32, 1, shape=(d.num_kv_heads,))
+    return k_scale, v_scale
 
 
 def dims(num_seqs, num_q_heads, k_pages: torch.Tensor, block_table: torch.Tensor) -> PaDims:
@@ -140,20 +196,24 @@ def kv_append(k_new, v_new, k_pages, v_pages, block_table, positions,
               seq_ids=None, k_scale=None, v_scale=None, num_seqs=None,
               stream=None):
     """Scatter k_new / v_new [T, Hkv, d] fp16 into the pages (see kv_append in the header)."""
-    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
-        _need(t, n, torch.float16, 3)
-    _need(k_pages, "k_pages", ndim=4); _need(v_pages, "v_pages", ndim=4)
+    _need(k_pages, "k_pages", ndim=4)
+    _need(v_pages, "v_pages", k_pages.dtype, 4, shape=k_pages.shape)
     _need(block_table, "block_table", torch.int32, 2)
-    _need(positions, "positions", torch.int32, 1)
-    if seq_ids is not None:
-        _need(seq_ids, "seq_ids", torch.int32, 1)
+    _need(k_new, "k_new", torch.float16, 3)
     T = k_new.shape[0]
     B = block_table.shape[0] if num_seqs is None else num_seqs
+    if B > block_table.shape[0]:
+        raise ValueError("num_seqs exceeds the block table's rows")
     d = dims(B, k_pages.shape[1], k_pages, block_table)
-    if k_new.shape != (T, d.num_kv_heads, d.head_dim) or v_new.shape != k_new.shape:
-        raise ValueError("k_new/v_new must be [T, Hkv, d]")
-    if positions.shape[0] != T or (seq_ids is not None and seq_ids.shape[0] != T):
-        raise ValueError("positions/seq_ids must have T entries")
+    _need(k_new, "k_new", shape=(T, d.num_kv_heads, d.head_dim))
+    _need(v_new, "v_new", torch.float16, 3, shape=k_new.shape)
+    _need(positions, "positions", torch.int32, 1, shape=(T,))
+    if seq_ids is not None:
+        _need(seq_ids, "seq_ids", torch.int32, 1, shape=(T,))
+    k_scale, v_scale = _scales(d, k_scale, v_scale)
+    _on_gpu(k_new=k_new, v_new=v_new, k_pages=k_pages, v_pages=v_pages,
+            block_table=block_table, positions=positions, seq_ids=seq_ids,
+            k_scale=k_scale, v_scale=v_scale)
     rc = load().kv_append(ctypes.byref(d), T, _ptr(k_new), _ptr(v_new),
                           _ptr(seq_ids), _ptr(positions), _ptr(block_table),
                           _ptr(k_scale), _ptr(v_scale), _ptr(k_pages),
@@ -162,29 +222,44 @@ def kv_append(k_new, v_new, k_pages, v_pages, block_table, positions,
 
 
 def _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale):
+    """Shapes and dtypes of an attention call's inputs; returns (dims,
+    k_scale, v_scale) with the scales None for an fp16 cache."""
     _need(q, "q", torch.float16, 3)
-    _need(k_pages, "k_pages", ndim=4); _need(v_pages, "v_pages", ndim=4)
-    _need(block_table, "block_table", torch.int32, 2)
-    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(k_pages, "k_pages", ndim=4)
+    _need(v_pages, "v_pages", k_pages.dtype, 4, shape=k_pages.shape)
     B, Hq, dq = q.shape
+    _need(block_table, "block_table", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1, shape=(B,))
     d = dims(B, Hq, k_pages, block_table)
-    P, Hkv, bs, hd = k_pages.shape
-    if v_pages.shape != k_pages.shape or v_pages.dtype != k_pages.dtype:
-        raise ValueError("v_pages must match k_pages' shape [P, Hkv, bs, d] and dtype")
-    if dq != hd or block_table.shape[0] != B or context_lens.shape[0] != B:
-        raise ValueError("inconsistent q / block_table / context_lens shapes")
-    if d.kv_dtype == KV_FP8_E4M3FN:
-        _need(k_scale, "k_scale", torch.float32, 1); _need(v_scale, "v_scale", torch.float32, 1)
-    return d
+    if dq != d.head_dim:
+        raise ValueError(f"q has head_dim {dq}, the pages {d.head_dim}")
+    if block_table.shape[0] != B:
+        raise ValueError(f"block_table has {block_table.shape[0]} rows, q {B} sequences")
+    ks, vs = _scales(d, k_scale, v_scale)
+    return d, ks, vs
+
+
+def _out(q, out):
+    """The fp16 output [B, Hq, d]: allocated like q, or checked against q."""
+    if out is None:
+        return torch.empty_like(q)
+    _need(out, "out", torch.float16, 3, shape=q.shape)
+    return out
+
+
+def _workspace_bytes(workspace):
+    _need(workspace, "workspace")
+    return workspace.numel() * workspace.element_size()
 
 
 def paged_decode_attn(q, k_pages, v_pages, block_table, context_lens, scale,
                       k_scale=None, v_scale=None, out=None, stream=None):
     """Single-pass decode attention; returns out [B, Hq, d] fp16."""
-    d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
-    if out is None:
-        out = torch.empty_like(q)
-    _need(out, "out", torch.float16, 3)
+    d, k_scale, v_scale = _attn_checks(q, k_pages, v_pages, block_table, context_lens,
+                                       k_scale, v_scale)
+    out = _out(q, out)
+    _on_gpu(q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table,
+            context_lens=context_lens, k_scale=k_scale, v_scale=v_scale, out=out)
     rc = load().paged_decode_attn(ctypes.byref(d), _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                   _ptr(block_table), _ptr(context_lens), float(scale),
                                   _ptr(k_scale), _ptr(v_scale), _ptr(out), _stream(stream))
@@ -206,12 +281,15 @@ def splitk_workspace(q, k_pages, block_table, num_splits):
 def paged_decode_attn_splitk(q, k_pages, v_pages, block_table, context_lens, scale,
                              num_splits, k_scale=None, v_scale=None, workspace=None,
                              stream=None):
-    """Split pass; returns the workspace (uint8 tensor holding o then lse)."""
-    d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
+    """Split pass; returns the workspace (uint8 tensor; see split_views)."""
+    d, k_scale, v_scale = _attn_checks(q, k_pages, v_pages, block_table, context_lens,
+                                       k_scale, v_scale)
     if workspace is None:
         workspace = splitk_workspace(q, k_pages, block_table, num_splits)
-    _need(workspace, "workspace")
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _workspace_bytes(workspace)
+    _on_gpu(q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table,
+            context_lens=context_lens, k_scale=k_scale, v_scale=v_scale,
+            workspace=workspace)
     rc = load().paged_decode_attn_splitk(ctypes.byref(d), _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                          _ptr(block_table), _ptr(context_lens), float(scale),
                                          _ptr(k_scale), _ptr(v_scale), int(num_splits),
@@ -223,13 +301,17 @@ def paged_decode_attn_splitk(q, k_pages, v_pages, block_table, context_lens, sca
 def paged_decode_attn_splitk_reduce(q_like, k_pages, block_table, context_lens,
                                     num_splits, workspace, out=None, stream=None):
     """Merge pass; q_like gives [B, Hq, d]. Returns out fp16."""
+    _need(q_like, "q_like", ndim=3)
     B, Hq, _ = q_like.shape
+    _need(k_pages, "k_pages", ndim=4)
+    _need(block_table, "block_table", torch.int32, 2)
     d = dims(B, Hq, k_pages, block_table)
-    _need(context_lens, "context_lens", torch.int32, 1)
+    _need(context_lens, "context_lens", torch.int32, 1, shape=(B,))
     if out is None:
         out = torch.empty(q_like.shape, dtype=torch.float16, device=q_like.device)
-    _need(out, "out", torch.float16, 3)
-    nbytes = workspace.numel() * workspace.element_size()
+    _need(out, "out", torch.float16, 3, shape=q_like.shape)
+    nbytes = _workspace_bytes(workspace)
+    _on_gpu(context_lens=context_lens, workspace=workspace, out=out)
     rc = load().paged_decode_attn_splitk_reduce(ctypes.byref(d), _ptr(context_lens),
                                                 int(num_splits), _ptr(workspace), nbytes,
                                                 _ptr(out), _stream(stream))
@@ -244,12 +326,13 @@ def paged_decode_attn_splitk_merged(q, k_pages, v_pages, block_table, context_le
 
     `workspace` must come from splitk_workspace() (its counters start at zero)
     and must not be shared by two merged calls running at the same time."""
-    d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
-    if out is None:
-        out = torch.empty_like(q)
-    _need(out, "out", torch.float16, 3)
-    _need(workspace, "workspace")
-    nbytes = workspace.numel() * workspace.element_size()
+    d, k_scale, v_scale = _attn_checks(q, k_pages, v_pages, block_table, context_lens,
+                                       k_scale, v_scale)
+    out = _out(q, out)
+    nbytes = _workspace_bytes(workspace)
+    _on_gpu(q=q, k_pages=k_pages, v_pages=v_pages, block_table=block_table,
+            context_lens=context_lens, k_scale=k_scale, v_scale=v_scale,
+            workspace=workspace, out=out)
     rc = load().paged_decode_attn_splitk_merged(
         ctypes.byref(d), _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
         _ptr(context_lens), float(scale), _ptr(k_scale), _ptr(v_scale), int(num_splits),
@@ -258,20 +341,29 @@ def paged_decode_attn_splitk_merged(q, k_pages, v_pages, block_table, context_le
     return out
 
 
+def _step_checks(q, k_new, v_new, positions, k_pages, v_pages, block_table,
+                 context_lens, k_scale, v_scale, out):
+    d, k_scale, v_scale = _attn_checks(q, k_pages, v_pages, block_table, context_lens,
+                                       k_scale, v_scale)
+    row = (d.num_seqs, d.num_kv_heads, d.head_dim)
+    _need(k_new, "k_new", torch.float16, 3, shape=row)
+    _need(v_new, "v_new", torch.float16, 3, shape=row)
+    _need(positions, "positions", torch.int32, 1, shape=(d.num_seqs,))
+    out = _out(q, out)
+    return d, k_scale, v_scale, out
+
+
 def paged_decode_step(q, k_new, v_new, positions, k_pages, v_pages, block_table,
                       context_lens, scale, num_splits, workspace, k_scale=None,
                       v_scale=None, out=None, stream=None):
     """kv_append of each sequence's new token (k_new/v_new [B, Hkv, d] fp16 at
     positions [B]) and the merged split attention, fused; returns out."""
-    d = _attn_checks(q, k_pages, v_pages, block_table, context_lens, k_scale, v_scale)
-    _need(k_new, "k_new", torch.float16, 3)
-    _need(v_new, "v_new", torch.float16, 3)
-    _need(positions, "positions", torch.int32, 1)
-    if out is None:
-        out = torch.empty_like(q)
-    _need(out, "out", torch.float16, 3)
-    _need(workspace, "workspace")
-    nbytes = workspace.numel() * workspace.element_size()
+    d, k_scale, v_scale, out = _step_checks(q, k_new, v_new, positions, k_pages, v_pages,
+                                            block_table, context_lens, k_scale, v_scale, out)
+    nbytes = _workspace_bytes(workspace)
+    _on_gpu(q=q, k_new=k_new, v_new=v_new, positions=positions, k_pages=k_pages,
+            v_pages=v_pages, block_table=block_table, context_lens=context_lens,
+            k_scale=k_scale, v_scale=v_scale, workspace=workspace, out=out)
     rc = load().paged_decode_step(
         ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions),
         _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(context_lens),
@@ -281,12 +373,37 @@ def paged_decode_step(q, k_new, v_new, positions, k_pages, v_pages, block_table,
     return out
 
 
+def paged_decode_advance(context_lens, positions, k_pages, block_table, stream=None):
+    """One decode step on, on the device: for every live slot (position >= 0)
+    positions and context_lens grow by one (see paged_decode_advance in the
+    header). Capturable after paged_decode_step in one graph."""
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    _need(positions, "positions", torch.int32, 1, shape=(B,))
+    _need(k_pages, "k_pages", ndim=4)
+    _need(block_table, "block_table", torch.int32, 2)
+    d = dims(B, k_pages.shape[1], k_pages, block_table)
+    _on_gpu(context_lens=context_lens, positions=positions)
+    rc = load().paged_decode_advance(ctypes.byref(d), _ptr(context_lens), _ptr(positions),
+                                     _stream(stream))
+    _check("paged_decode_advance", rc)
+
+
 def split_views(workspace, B, Hq, Hkv, S, D):
-    """(o [B,Hq,S,D] f32, lse [B,Hq,S] f32, count [B,Hkv] i32) views of a workspace."""
+    """(o [B,Hq,S,D] f32, lse [B,Hq,S] f32, count [B,Hkv] i32) views of a
+    workspace (uint8 tensor), in the header's layout: the arrival counters
+    first (sem_view), then o, lse and count."""
     n = B * Hq * S
-    f = workspace[:(n * D + n) * 4].view(torch.float32)
-    c = workspace[(n * D + n) * 4:(n * D + n) * 4 + B * Hkv * 4].view(torch.int32)
+    base = WORKSPACE_SEM_SLOTS * 4
+    f = workspace[base:base + (n * D + n) * 4].view(torch.float32)
+    c = workspace[base + (n * D + n) * 4:base + (n * D + n) * 4 + B * Hkv * 4].view(torch.int32)
     return f[:n * D].view(B, Hq, S, D), f[n * D:].view(B, Hq, S), c.view(B, Hkv)
+
+
+def sem_view(workspace):
+    """The merged call's arrival counters (int32 [WORKSPACE_SEM_SLOTS]):
+    zero between calls."""
+    return workspace[:WORKSPACE_SEM_SLOTS * 4].view(torch.int32)
 
 
 def suggest_splits(d: PaDims, max_context_len: int) -> int:
@@ -298,3 +415,7 @@ def step_fuses_append(d: PaDims) -> bool:
     rc = int(load().paged_decode_step_fuses_append(ctypes.byref(d)))
     _check("paged_decode_step_fuses_append", min(rc, 0))
     return rc == 1
+
+
+from .kv_manager import (KvPageManager, kv_bytes_per_sequence,  # noqa: E402
+                         kv_pages_for_budget, kv_pool_bytes)

@@ -17,7 +17,13 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "lib")
 LIB_NAME = "libpagedattn.so"
-SOURCES = ["api.hip", "kv_append.hip", "decode_attn.hip", "splitk_reduce.hip"]
+# (source, object name, extra defines). The attention kernels are compiled
+# once per (cache kind, head_dim) pair, so their instances build in parallel.
+SOURCES = [("api.hip", "api", []), ("kv_append.hip", "kv_append", []),
+           ("splitk_reduce.hip", "splitk_reduce", []),
+           ("kv_manager.cpp", "kv_manager", [])] + [
+    ("decode_attn.hip", f"decode_attn_{kind}_d{d}", [f"-DPA_INST_KV={kv}", f"-DPA_INST_D={d}"])
+    for kv, kind in ((0, "f16"), (1, "f8"), (2, "i8")) for d in (64, 128)]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [
@@ -35,22 +41,31 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, obj: str) -> tuple[str, int, str]:
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-only C++ (the page manager): built by the same driver without device
+# code, as plain C++17.
+HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE,
+              "-I", CSRC]
+
+
+def _compile(item, obj_dir: str) -> tuple[str, int, str]:
+    src, name, defines = item
+    obj = os.path.join(obj_dir, name + ".o")
+    flags = HOST_FLAGS if src.endswith(".cpp") else COMMON_FLAGS
+    cmd = [hipcc(), *flags, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (p.stdout + p.stderr).splitlines()
                     if "packed-fp32-ops" not in l and "not a recognized feature" not in l)
-    return src, p.returncode, err
+    return name, p.returncode, err
 
 
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     """Compile every HIP source and link the shared library; returns its path."""
     obj_dir = os.path.join(OUT_DIR, "obj")
     os.makedirs(obj_dir, exist_ok=True)
-    objs = [os.path.join(obj_dir, s.replace(".hip", ".o")) for s in SOURCES]
+    objs = [os.path.join(obj_dir, name + ".o") for _, name, _ in SOURCES]
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4, 16)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, SOURCES, objs))
+        results = list(ex.map(lambda it: _compile(it, obj_dir), SOURCES))
     failed = [(s, e) for s, rc, e in results if rc != 0]
     for s, rc, e in results:
         if verbose and e.strip():

@@ -8,6 +8,24 @@
 
 #include "launch.h"
 
+namespace pa {
+
+hipError_t launch_attn(const AttnArgs& a, int D, int BS, int kv, hipStream_t st) {
+  if (D == 64) {
+    if (kv == kKvF8) return launch_attn_inst<kKvF8, 64>(a, BS, st);
+    if (kv == kKvI8) return launch_attn_inst<kKvI8, 64>(a, BS, st);
+    return launch_attn_inst<kKvF16, 64>(a, BS, st);
+  }
+  if (D == 128) {
+    if (kv == kKvF8) return launch_attn_inst<kKvF8, 128>(a, BS, st);
+    if (kv == kKvI8) return launch_attn_inst<kKvI8, 128>(a, BS, st);
+    return launch_attn_inst<kKvF16, 128>(a, BS, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
+
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -25,14 +43,25 @@ int check_dims(const pa_dims* d) {
   if ((long long)d->max_blocks_per_seq * d->block_size > INT_MAX)
     return PA_ERR_SHAPE;
   if ((long long)d->num_pages * d->num_kv_heads > INT_MAX) return PA_ERR_SHAPE;
-  if (d->kv_dtype != PA_KV_FP16 && d->kv_dtype != PA_KV_FP8_E4M3FN)
+  if (d->kv_dtype != PA_KV_FP16 && d->kv_dtype != PA_KV_FP8_E4M3FN &&
+      d->kv_dtype != PA_KV_INT8)
     return PA_ERR_DTYPE;
   return PA_OK;
 }
 
+// One-byte caches need their per-kv-head K and V scales.
 int check_scales(const pa_dims* d, const float* ks, const float* vs) {
-  if (d->kv_dtype == PA_KV_FP8_E4M3FN && (!ks || !vs)) return PA_ERR_DTYPE;
+  if (d->kv_dtype != PA_KV_FP16 && (!ks || !vs)) return PA_ERR_DTYPE;
   return PA_OK;
+}
+
+// The kernels' cache kind (pa::KvKind) of a pa_kv_dtype.
+int kv_kind(const pa_dims* d) {
+  switch (d->kv_dtype) {
+    case PA_KV_FP8_E4M3FN: return pa::kKvF8;
+    case PA_KV_INT8: return pa::kKvI8;
+    default: return pa::kKvF16;
+  }
 }
 
 pa::AttnArgs make_args(const pa_dims* d, const void* q, const void* kp,
@@ -70,12 +99,18 @@ void apply_fuse(pa::AttnArgs& a, const Fuse* f) {
   a.positions = f->positions;
 }
 
-// Workspace: o f32 [B, Hq, S, D], lse f32 [B, Hq, S], count i32 [B, Hkv],
-// sem i32 [B, Hkv].
+// Workspace: sem i32 [PA_WORKSPACE_SEM_SLOTS] at a fixed offset (the merged
+// call's arrival counters, left zero by every completed call, so a
+// workspace can serve calls of any size in turn), then o f32 [B, Hq, S, D],
+// lse f32 [B, Hq, S], count i32 [B, Hkv].
+static_assert(PA_WORKSPACE_SEM_SLOTS >= pa::kMaxStreamWorkers,
+              "one arrival counter per split-pass worker");
+constexpr size_t kSemBytes = PA_WORKSPACE_SEM_SLOTS * sizeof(int32_t);
+
 size_t ws_bytes(const pa_dims* d, int32_t S) {
   const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
-  return rows * (size_t)d->head_dim * sizeof(float) + rows * sizeof(float) +
-         2 * (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
+  return kSemBytes + rows * (size_t)d->head_dim * sizeof(float) +
+         rows * sizeof(float) + (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
 }
 
 struct WsViews {
@@ -88,58 +123,15 @@ struct WsViews {
 WsViews ws_views(const pa_dims* d, int32_t S, void* ws) {
   const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
   WsViews v;
-  v.o = static_cast<float*>(ws);
+  v.sem = static_cast<int32_t*>(ws);
+  v.o = reinterpret_cast<float*>(static_cast<char*>(ws) + kSemBytes);
   v.lse = v.o + rows * d->head_dim;
   v.count = reinterpret_cast<int32_t*>(v.lse + rows);
-  v.sem = v.count + (size_t)d->num_seqs * d->num_kv_heads;
   return v;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-}  // namespace
-
-extern "C" {
-
-int kv_append(const pa_dims* dims, int32_t num_tokens, const void* k_new,
-              const void* v_new, const int32_t* seq_ids,
-              const int32_t* positions, const int32_t* block_table,
-              const float* k_scale, const float* v_scale, void* k_pages,
-              void* v_pages, hipStream_t stream) {
-  int rc = check_dims(dims);
-  if (rc) return rc;
-  if (num_tokens < 0) return PA_ERR_SHAPE;
-  if (!seq_ids && num_tokens > dims->num_seqs) return PA_ERR_SHAPE;
-  if ((long long)num_tokens * dims->num_kv_heads * (dims->head_dim / 2) >
-      (long long)INT_MAX * 256)
-    return PA_ERR_SHAPE;
-  if (!k_new || !v_new || !positions || !block_table || !k_pages || !v_pages)
-    return PA_ERR_NULL;
-  rc = check_scales(dims, k_scale, v_scale);
-  if (rc) return rc;
-  if (num_tokens == 0 || dims->num_seqs == 0) return PA_OK;
-  pa::KvAppendArgs a{};
-  a.k_new = static_cast<const uint8_t*>(k_new);
-  a.v_new = static_cast<const uint8_t*>(v_new);
-  a.seq_ids = seq_ids;
-  a.positions = positions;
-  a.block_table = block_table;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.k_pages = static_cast<uint8_t*>(k_pages);
-  a.v_pages = static_cast<uint8_t*>(v_pages);
-  a.num_tokens = num_tokens;
-  a.B = dims->num_seqs;
-  a.Hkv = dims->num_kv_heads;
-  a.bs = dims->block_size;
-  a.P = dims->num_pages;
-  a.max_blocks = dims->max_blocks_per_seq;
-  return hip_status(pa::launch_kv_append(a, dims->head_dim,
-                                         dims->kv_dtype == PA_KV_FP8_E4M3FN,
-                                         stream));
-}
-
-namespace {
 
 int single_impl(const pa_dims* dims, const void* q, const void* k_pages,
                 const void* v_pages, const int32_t* block_table,
@@ -161,28 +153,9 @@ int single_impl(const pa_dims* dims, const void* q, const void* k_pages,
   a.mode = 0;
   apply_fuse(a, fuse);
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
-                                    dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+                                    kv_kind(dims), stream));
 }
 
-}  // namespace
-
-int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
-                      const void* v_pages, const int32_t* block_table,
-                      const int32_t* context_lens, float scale,
-                      const float* k_scale, const float* v_scale, void* out,
-                      hipStream_t stream) {
-  return single_impl(dims, q, k_pages, v_pages, block_table, context_lens,
-                     scale, k_scale, v_scale, out, stream, nullptr);
-}
-
-size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
-                                               int32_t num_splits) {
-  if (check_dims(dims) != PA_OK) return 0;
-  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return 0;
-  return ws_bytes(dims, num_splits);
-}
-
-namespace {
 
 int split_impl(const pa_dims* dims, const void* q, const void* k_pages,
                const void* v_pages, const int32_t* block_table,
@@ -212,21 +185,7 @@ int split_impl(const pa_dims* dims, const void* q, const void* k_pages,
   a.mode = num_splits == 1 ? 1 : 2;
   apply_fuse(a, fuse);
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
-                                    dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
-}
-
-}  // namespace
-
-int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
-                             const void* k_pages, const void* v_pages,
-                             const int32_t* block_table,
-                             const int32_t* context_lens, float scale,
-                             const float* k_scale, const float* v_scale,
-                             int32_t num_splits, void* workspace,
-                             size_t workspace_bytes, hipStream_t stream) {
-  return split_impl(dims, q, k_pages, v_pages, block_table, context_lens, scale,
-                    k_scale, v_scale, num_splits, workspace, workspace_bytes,
-                    stream, nullptr);
+                                    kv_kind(dims), stream));
 }
 
 // Largest group size (q heads per kv head) whose partials the merged call
@@ -240,8 +199,6 @@ constexpr int kMergeInKernelMaxGroup = 16;
 // separate append launch (measured on MI355X: fused ahead by 2-14 us up to
 // 1024 pairs, behind by 1-9 us at 2048).
 constexpr long long kFuseAppendMaxPairs = 1536;
-
-namespace {
 
 // Argument checks of the merged call, all done before anything is launched.
 int check_merged(const pa_dims* dims, const void* q, const void* k_pages,
@@ -300,10 +257,81 @@ int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
   a.mode = 3;
   apply_fuse(a, fuse);
   return hip_status(pa::launch_attn(a, dims->head_dim, dims->block_size,
-                                    dims->kv_dtype == PA_KV_FP8_E4M3FN, stream));
+                                    kv_kind(dims), stream));
 }
 
 }  // namespace
+
+extern "C" {
+
+int kv_append(const pa_dims* dims, int32_t num_tokens, const void* k_new,
+              const void* v_new, const int32_t* seq_ids,
+              const int32_t* positions, const int32_t* block_table,
+              const float* k_scale, const float* v_scale, void* k_pages,
+              void* v_pages, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (num_tokens < 0) return PA_ERR_SHAPE;
+  if (!seq_ids && num_tokens > dims->num_seqs) return PA_ERR_SHAPE;
+  if ((long long)num_tokens * dims->num_kv_heads * (dims->head_dim / 2) >
+      (long long)INT_MAX * 256)
+    return PA_ERR_SHAPE;
+  if (!k_new || !v_new || !positions || !block_table || !k_pages || !v_pages)
+    return PA_ERR_NULL;
+  rc = check_scales(dims, k_scale, v_scale);
+  if (rc) return rc;
+  if (num_tokens == 0 || dims->num_seqs == 0) return PA_OK;
+  pa::KvAppendArgs a{};
+  a.k_new = static_cast<const uint8_t*>(k_new);
+  a.v_new = static_cast<const uint8_t*>(v_new);
+  a.seq_ids = seq_ids;
+  a.positions = positions;
+  a.block_table = block_table;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.k_pages = static_cast<uint8_t*>(k_pages);
+  a.v_pages = static_cast<uint8_t*>(v_pages);
+  a.num_tokens = num_tokens;
+  a.B = dims->num_seqs;
+  a.Hkv = dims->num_kv_heads;
+  a.bs = dims->block_size;
+  a.P = dims->num_pages;
+  a.max_blocks = dims->max_blocks_per_seq;
+  return hip_status(pa::launch_kv_append(a, dims->head_dim, kv_kind(dims), stream));
+}
+
+
+int paged_decode_attn(const pa_dims* dims, const void* q, const void* k_pages,
+                      const void* v_pages, const int32_t* block_table,
+                      const int32_t* context_lens, float scale,
+                      const float* k_scale, const float* v_scale, void* out,
+                      hipStream_t stream) {
+  return single_impl(dims, q, k_pages, v_pages, block_table, context_lens,
+                     scale, k_scale, v_scale, out, stream, nullptr);
+}
+
+size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
+                                               int32_t num_splits) {
+  if (check_dims(dims) != PA_OK) return 0;
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return 0;
+  return ws_bytes(dims, num_splits);
+}
+
+
+int paged_decode_attn_splitk(const pa_dims* dims, const void* q,
+                             const void* k_pages, const void* v_pages,
+                             const int32_t* block_table,
+                             const int32_t* context_lens, float scale,
+                             const float* k_scale, const float* v_scale,
+                             int32_t num_splits, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return split_impl(dims, q, k_pages, v_pages, block_table, context_lens, scale,
+                    k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                    stream, nullptr);
+}
+
+// Largest group size (q heads per kv head) whose partials the merged call
+// merges inside the attention kernel.
 
 int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
                                     const void* k_pages, const void* v_pages,
@@ -377,6 +405,17 @@ int paged_decode_attn_splitk_reduce(const pa_dims* dims,
   return hip_status(pa::launch_reduce(a, dims->head_dim, stream));
 }
 
+
+int paged_decode_advance(const pa_dims* dims, int32_t* context_lens, int32_t* positions,
+                         hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!context_lens || !positions) return PA_ERR_NULL;
+  if (dims->num_seqs == 0) return PA_OK;
+  return hip_status(pa::launch_advance(context_lens, positions, dims->num_seqs,
+                                       dims->max_blocks_per_seq * dims->block_size, stream));
+}
+
 int32_t paged_decode_step_fuses_append(const pa_dims* dims) {
   const int rc = check_dims(dims);
   if (rc) return rc;
@@ -388,12 +427,12 @@ int32_t paged_decode_attn_suggest_splits(const pa_dims* dims,
   if (check_dims(dims) != PA_OK || max_context_len <= 0) return 1;
   // The split pass spreads the batch's 32-token tiles evenly over a
   // persistent grid of W workers (<= 16 q heads per kv head: 1024 for fp16,
-  // 2048 for fp8; 1024 up to 64; else 512); the longest (sequence, kv head)
+  // 2048 for one-byte caches; 1024 up to 64; else 512); the longest (sequence, kv head)
   // then spans about
   // n_max * W / T + 1 of them. Assuming the batch's mean context is at
   // least 1/16 of the longest (T >= pairs * n_max / 16) gives the bound.
   const int G = dims->num_q_heads / dims->num_kv_heads;
-  const long long W = G <= 16 ? (dims->kv_dtype == PA_KV_FP8_E4M3FN ? 2048 : 1024)
+  const long long W = G <= 16 ? (dims->kv_dtype != PA_KV_FP16 ? 2048 : 1024)
                               : (G <= 64 ? 1024 : 512);
   const long long tiles = (max_context_len + 31) / 32;
   const long long pairs = (long long)dims->num_seqs * dims->num_kv_heads;

@@ -15,7 +15,8 @@
 //    HBM into MFMA operand registers, the next tile's loads in flight while
 //    the current tile is computed. The page layout stores each 16-token
 //    block in operand order, so every wave-wide load reads whole 128-byte
-//    lines and a lane's V operand is one 16-byte (fp8: 8-byte) run.
+//    lines and a lane's V operand is one 16-byte (one-byte codes: 8-byte)
+//    run.
 //  * QK^T: 16 tokens of the tile as the A operand (16 tokens x 32 dims),
 //    the group's q heads as B (32 dims x 16 heads). The 16x16 result holds,
 //    per lane, scores of one head for 4 tokens; the two token halves of a
@@ -30,9 +31,10 @@
 //  * Page ids are clamped into the pool; tokens past the end re-read a
 //    valid block and are masked by select, so NaN in unused slots never
 //    leaks.
-//  * fp8 e4m3fn K/V are expanded to fp16 in registers by bit placement
-//    (value * 2^-8, exact); 2^8 and the per-head scales fold into the score
-//    scale and the final output scale.
+//  * One-byte K/V codes are expanded to fp16 in registers by exact bit
+//    placement (fp8 e4m3fn: value * 2^-8; int8: the integer itself); the
+//    code unit (2^8 or 1) and the per-head scales fold into the score scale
+//    and the final output scale.
 //  * Two schedules. Single pass: one workgroup per (sequence, kv head), its
 //    token-parallel waves merged through LDS. Split pass (stream-K): every
 //    wave (or head-parallel wave group) is a worker; the tiles of all
@@ -53,9 +55,10 @@ constexpr int kTile = 32;       // tokens per tile
 constexpr float kLazyLog2 = 8.0f;  // headroom of the lazy softmax rescale
 constexpr int kMaxPages = 512;  // page ids staged in LDS per chunk (single pass)
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, int KV>
 struct Geo {
-  static constexpr int kEsz = FP8 ? 1 : 2;
+  static constexpr bool kByte = KV != kKvF16;        // one-byte codes
+  static constexpr int kEsz = kByte ? 1 : 2;
   static constexpr int kRowBytes = D * kEsz;          // one token row
   static constexpr int kBlockBytes = 16 * kRowBytes;  // one 16-token block
   static constexpr int kPageBytes = BS * D * kEsz;    // one (page, head) tile
@@ -65,11 +68,11 @@ struct Geo {
 };
 
 // First dimension of the 8 K-slots that lane group g (= lane / 16) holds in
-// QK MFMA number jj. fp16: a 16 B K chunk covers one MFMA; fp8: a 16 B chunk
-// covers 16 dims, i.e. two MFMAs.
-template <bool FP8>
+// QK MFMA number jj. fp16: a 16 B K chunk covers one MFMA; one-byte codes: a
+// 16 B chunk covers 16 dims, i.e. two MFMAs.
+template <bool BYTE>
 __device__ __forceinline__ int kslot_dim(int jj, int g) {
-  return FP8 ? 64 * (jj >> 1) + 16 * g + 8 * (jj & 1) : 32 * jj + 8 * g;
+  return BYTE ? 64 * (jj >> 1) + 16 * g + 8 * (jj & 1) : 32 * jj + 8 * g;
 }
 
 template <bool NT, typename T>
@@ -78,12 +81,12 @@ __device__ __forceinline__ T load16(const T* p) {
   else return *p;
 }
 
-template <int D, int BS, bool FP8>
+template <int D, int BS, int KV>
 struct TileRegs {
-  using G = Geo<D, BS, FP8>;
+  using G = Geo<D, BS, KV>;
   // V operand of one 16-dim group: the lane's 8 tokens of one dimension,
   // one contiguous run in the page
-  using VT = typename std::conditional<FP8, u32x2, u32x4>::type;
+  using VT = typename std::conditional<G::kByte, u32x2, u32x4>::type;
   u32x4 k[2][G::kKLoads];      // [QK MFMA m][chunk group]
   VT v[G::kPvMfma];            // [16-dim group]
 };
@@ -107,12 +110,12 @@ struct TileRegs {
 // instruction at one line of the tile given by off0 (the tile just loaded):
 // 16 lines per wave instead of a whole tile re-read. (One shared address for
 // every wave would pile all waves' dead loads onto one memory channel.)
-template <int D, int BS, bool FP8, bool NT>
-__device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
+template <int D, int BS, int KV, bool NT>
+__device__ __forceinline__ void load_tile(TileRegs<D, BS, KV>& t,
                                           const uint8_t* kbase,
                                           const uint8_t* vbase, long long off0,
                                           long long off1, int lane, bool live) {
-  using Gm = Geo<D, BS, FP8>;
+  using Gm = Geo<D, BS, KV>;
   const int R = lane & 15, lg = lane >> 4;
   if (!live) off1 = off0;
   const int klane = live ? (lg * 16 + (R & 7)) * 16 : 0;
@@ -127,7 +130,7 @@ __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
 #pragma unroll
   for (int jd = 0; jd < Gm::kPvMfma; ++jd)
     t.v[jd] = load16<NT>(
-        reinterpret_cast<const typename TileRegs<D, BS, FP8>::VT*>(vb + jd * 256 * Gm::kEsz));
+        reinterpret_cast<const typename TileRegs<D, BS, KV>::VT*>(vb + jd * 256 * Gm::kEsz));
 }
 
 // Attention state of one wave for NH blocks of 16 q heads of one (sequence,
@@ -135,10 +138,10 @@ __device__ __forceinline__ void load_tile(TileRegs<D, BS, FP8>& t,
 // with QL in this wave's LDS region `qsh` ([NH][d/32][64 lanes] of 16 bytes,
 // read back conflict-free), which leaves the registers to the accumulators
 // of wide groups.
-template <int D, int BS, bool FP8, int NH, bool QL = false>
+template <int D, int BS, int KV, int NH, bool QL = false>
 struct HeadState {
-  using Gm = Geo<D, BS, FP8>;
-  using Tile = TileRegs<D, BS, FP8>;
+  using Gm = Geo<D, BS, KV>;
+  using Tile = TileRegs<D, BS, KV>;
   half8 qop[QL ? 1 : NH][Gm::kQkMfma];
   u32x4* qsh;
   float mrun[NH], lrun[NH];
@@ -151,9 +154,9 @@ struct HeadState {
                                         int mrow, int lg) {
     sl = a.scale_log2;
     oscale = 1.0f;
-    if constexpr (FP8) {
-      sl *= load_uniform(a.k_scale + h) * 256.0f;
-      oscale = load_uniform(a.v_scale + h) * 256.0f;
+    if constexpr (Gm::kByte) {
+      sl *= load_uniform(a.k_scale + h) * code_unit<KV>();
+      oscale = load_uniform(a.v_scale + h) * code_unit<KV>();
     }
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
@@ -162,7 +165,7 @@ struct HeadState {
       const _Float16* qrow = a.q + ((long long)b * a.Hq + h * a.G + (ok ? gh : 0)) * D;
 #pragma unroll
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kslot_dim<FP8>(jj, lg));
+        u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kslot_dim<Gm::kByte>(jj, lg));
         if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
         if constexpr (QL) qsh[(hb * Gm::kQkMfma + jj) * 64 + __lane_id()] = raw;
         else qop[hb][jj] = as_half8(raw);
@@ -184,10 +187,10 @@ struct HeadState {
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
-        if constexpr (FP8) {
+        if constexpr (Gm::kByte) {
           const u32x4 w = t.k[m][jj >> 1];
           const u32x2 hlf = (jj & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
-          kop[m][jj] = e4m3x8_to_half8(hlf);
+          kop[m][jj] = codes8_to_half8<KV>(hlf);
         } else {
           kop[m][jj] = as_half8(t.k[m][jj]);
         }
@@ -197,7 +200,7 @@ struct HeadState {
     if (tail) {
       // zero the V entries of tokens past the end, in place (a masked
       // probability of 0 times a NaN left in an unused slot is still NaN)
-      auto keep8 = [](int n) {        // fp8: bytes of the first n tokens
+      auto keep8 = [](int n) {        // one-byte codes of the first n tokens
         return n <= 0 ? 0u : (n >= 4 ? 0xFFFFFFFFu : (1u << (8 * n)) - 1u);
       };
       auto keep16 = [](int n, int w) {   // fp16: halves of tokens 2w, 2w+1
@@ -205,7 +208,7 @@ struct HeadState {
       };
 #pragma unroll
       for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-        if constexpr (FP8) {
+        if constexpr (Gm::kByte) {
           t.v[jd].x &= keep8(nv);
           t.v[jd].y &= keep8(nv - 4);
         } else {
@@ -219,7 +222,7 @@ struct HeadState {
     half8 vop[Gm::kPvMfma];
 #pragma unroll
     for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-      if constexpr (FP8) vop[jd] = e4m3x8_to_half8(t.v[jd]);
+      if constexpr (Gm::kByte) vop[jd] = codes8_to_half8<KV>(t.v[jd]);
       else vop[jd] = as_half8(t.v[jd]);
     }
 #pragma unroll
@@ -353,10 +356,10 @@ __device__ __forceinline__ int clamp_page(int p, int P) {
 
 // Fused append: write the new token of (sequence b, kv head h) at position p
 // into its page (one wave, two dimensions per lane), as kv_append does.
-template <int D, int BS, bool FP8>
+template <int D, int BS, int KV>
 __device__ __forceinline__ void append_token(const AttnArgs& a, int b, int h,
                                              int p, int lane) {
-  constexpr int kEsz = FP8 ? 1 : 2;
+  constexpr int kEsz = KV != kKvF16 ? 1 : 2;
   const int page = clamp_page(
       load_uniform(a.block_table + (long long)b * a.max_blocks + p / BS), a.P);
   const long long tile = ((long long)page * a.Hkv + h) * BS * D * kEsz;
@@ -367,11 +370,11 @@ __device__ __forceinline__ void append_token(const AttnArgs& a, int b, int h,
     const uint32_t kin = *reinterpret_cast<const uint32_t*>(a.k_new + row + dp);
     const uint32_t vin = *reinterpret_cast<const uint32_t*>(a.v_new + row + dp);
     float ks = 1.0f, vs = 1.0f;
-    if constexpr (FP8) {
+    if constexpr (KV != kKvF16) {
       ks = load_uniform(a.k_scale + h);
       vs = load_uniform(a.v_scale + h);
     }
-    store_kv_pair<D, FP8>(kt, vt, p % BS, dp, kin, vin, ks, vs);
+    store_kv_pair<D, KV>(kt, vt, p % BS, dp, kin, vin, ks, vs);
   }
 }
 
@@ -388,12 +391,12 @@ struct SharedMem {
   float acc[TW > 1 ? TW - 1 : 1][kHeads][D];
 };
 
-template <int D, int BS, bool FP8, int NH, int NWH, int TW>
+template <int D, int BS, int KV, int NH, int NWH, int TW>
 __global__ __launch_bounds__(64 * NWH * TW)
 __attribute__((amdgpu_waves_per_eu(NH == 1 ? 2 : 1)))
 void decode_attn_kernel(AttnArgs a) {
-  using Gm = Geo<D, BS, FP8>;
-  using Tile = TileRegs<D, BS, FP8>;
+  using Gm = Geo<D, BS, KV>;
+  using Tile = TileRegs<D, BS, KV>;
   using Smem = SharedMem<NH, NWH, TW, D>;
   __shared__ Smem sm;
   const int lane = threadIdx.x & 63;
@@ -409,12 +412,12 @@ void decode_attn_kernel(AttnArgs a) {
     // workgroup's other waves
     if (wave == 0) {
       const int p = load_uniform(a.positions + b);
-      if (p >= 0 && p < a.max_blocks * BS) append_token<D, BS, FP8>(a, b, h, p, lane);
+      if (p >= 0 && p < a.max_blocks * BS) append_token<D, BS, KV>(a, b, h, p, lane);
       wait_vector_memory();
     }
     __syncthreads();
   }
-  HeadState<D, BS, FP8, NH> st;
+  HeadState<D, BS, KV, NH> st;
   st.begin(a, b, h, hw, mrow, lg);
   const uint8_t* kbase = a.k_pages + (long long)h * Gm::kPageBytes;
   const uint8_t* vbase = a.v_pages + (long long)h * Gm::kPageBytes;
@@ -440,7 +443,7 @@ void decode_attn_kernel(AttnArgs a) {
         const int tb = min(ts + 16 * r, last_blk);
         off[r] = sm.pages[tb / BS - p0] * page_stride + (tb % BS) * Gm::kRowBytes;
       }
-      load_tile<D, BS, FP8, NWH == 1>(t, kbase, vbase, off[0], off[1], lane, live);
+      load_tile<D, BS, KV, NWH == 1>(t, kbase, vbase, off[0], off[1], lane, live);
     };
     // Two register tiles in flight; the next tile's loads are issued on
     // every iteration, unconditionally (past the last tile as dead loads),
@@ -611,10 +614,10 @@ __device__ __forceinline__ Cursor locate(const AttnArgs& a, long long x, int cap
 
 // Byte offsets (head included) of the two 16-token blocks of c's tile. A
 // block wholly past the end re-reads the first one (in bounds; masked).
-template <int D, int BS, bool FP8>
+template <int D, int BS, int KV>
 __device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
                                              long long& off0, long long& off1) {
-  using Gm = Geo<D, BS, FP8>;
+  using Gm = Geo<D, BS, KV>;
   const int* bt_row = a.block_table + (long long)c.b * a.max_blocks;
   const long long page_stride = (long long)a.Hkv * Gm::kPageBytes;
   const long long head = (long long)c.h * Gm::kPageBytes;
@@ -726,17 +729,17 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
 // count unless that would cut some (sequence, kv head) into more than S
 // ranges (checked exactly), in which case W is lowered until
 // floor(T / W) >= ceil(n_max / (S - 1)), which bounds every pair by S
-// ranges. mode 2 writes the
-// partials and their count; mode 3 merges too: a (sequence, kv head) held
-// by one worker is written out directly, otherwise the last of its workers
-// to finish (an atomic counter per (sequence, kv head), returned to zero
-// afterwards) merges the partials.
-template <int D, int BS, bool FP8, int NH, int NWH, bool QL, int SLOTS>
+// ranges. mode 2 writes the partials and their count; mode 3 merges too: a
+// (sequence, kv head) held by one worker is written out directly, otherwise
+// the last of its workers to finish merges the partials (an atomic arrival
+// counter per pair, kept at the index of the pair's first worker and
+// returned to zero afterwards).
+template <int D, int BS, int KV, int NH, int NWH, bool QL, int SLOTS>
 __global__ __launch_bounds__(NH == 1 && SLOTS == 2 ? 512 : 256)
 __attribute__((amdgpu_waves_per_eu(NH == 1 && SLOTS == 2 ? 2 : 1)))
 void decode_attn_stream_kernel(AttnArgs a) {
-  using Tile = TileRegs<D, BS, FP8>;
-  using Gm = Geo<D, BS, FP8>;
+  using Tile = TileRegs<D, BS, KV>;
+  using Gm = Geo<D, BS, KV>;
   // one 8-wave workgroup per CU (two waves per SIMD) for the small
   // two-tile configuration, else one wave per SIMD
   constexpr int kWaves = NH == 1 && SLOTS == 2 ? 8 : 4;
@@ -801,7 +804,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
       if (a.k_new != nullptr) {
         const int p = load_uniform(a.positions + b);
         if (p >= 0 && p < cap)
-          for (int h = 0; h < a.Hkv; ++h) append_token<D, BS, FP8>(a, b, h, p, lane);
+          for (int h = 0; h < a.Hkv; ++h) append_token<D, BS, KV>(a, b, h, p, lane);
       }
     }
   }
@@ -820,7 +823,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
   if (c.base < r0) fw = uniform(((c.base + 1) * W - 1) / T);
   if (e.base + e.n > r1) lw = uniform(((e.base + e.n) * W - 1) / T);
 
-  HeadState<D, BS, FP8, NH, QL> st;
+  HeadState<D, BS, KV, NH, QL> st;
   st.qsh = qsmem[wave];
   st.begin(a, c.b, c.h, hw, mrow, lg);         // q loads overlap the append
 
@@ -835,7 +838,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     auto append_if_here = [&](const Cursor& s, int p) {
       if (p < 0 || p >= cap) return;
       const long long tp = s.base + min(p / kTile, s.n - 1);
-      if (tp >= r0 && tp < r1) append_token<D, BS, FP8>(a, s.b, s.h, p, lane);
+      if (tp >= r0 && tp < r1) append_token<D, BS, KV>(a, s.b, s.h, p, lane);
     };
     const int pc = load_uniform(a.positions + c.b);
     const int pe = load_uniform(a.positions + e.b);
@@ -881,22 +884,30 @@ void decode_attn_stream_kernel(AttnArgs a) {
     // makes them visible to whichever compute unit merges, which reads them
     // with device-scope atomic loads. (A release/acquire pair would instead
     // write back and invalidate the whole L2 of the XCD at every arrival.)
+    // The counter of a pair is indexed by the pair's first worker: a worker
+    // is the first of at most one pair that extends past its share (its
+    // last pair), so the counters sit at a fixed place whatever the batch.
     st.template write_rows<true>(a, s.b, s.h, hw, slot, mrow, lg);
+    compiler_fence();
     wait_vector_memory();
+    compiler_fence();
     int old = 0;
+    int* sem = a.ws_sem + first;
     if (lane == 0)
-      old = __hip_atomic_fetch_add(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 1,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = uniform(__shfl(old, 0, 64));
     const int arrivals = (int)(last - first + 1) * NWH;
     if (old == arrivals - 1) {
+      // the other workers' partials: visible at the device-coherent level
+      // (their stores completed before their increments); read past this
+      // CU's caches by the device-scope loads of the merge
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       if constexpr (decltype(at_end)::value)
         merge_partials<D, 2>(a, s.b, s.h, (int)(last - first + 1), lane);
       else
         merge_partials<D, 1>(a, s.b, s.h, (int)(last - first + 1), lane);
       if (lane == 0)
-        __hip_atomic_store(&a.ws_sem[(long long)s.b * a.Hkv + s.h], 0,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
@@ -907,8 +918,8 @@ void decode_attn_stream_kernel(AttnArgs a) {
   constexpr bool kNT = NWH == 1;
   if constexpr (SLOTS == 2) {
     Tile ta, tb;
-    tile_offsets<D, BS, FP8>(a, c, o0, o1);
-    load_tile<D, BS, FP8, kNT>(ta, kp, vp, o0, o1, lane, true);
+    tile_offsets<D, BS, KV>(a, c, o0, o1);
+    load_tile<D, BS, KV, kNT>(ta, kp, vp, o0, o1, lane, true);
     // One pipeline over the whole share: the next tile's loads (even in the
     // next segment) are in flight while the current tile is computed. They
     // are issued unconditionally (past the share's end as dead loads) so
@@ -916,8 +927,8 @@ void decode_attn_stream_kernel(AttnArgs a) {
     auto iter = [&](Tile& cur, Tile& nxt) {
       const bool more = pos + 1 < r1;
       const Cursor nx = more ? advance(a, c, cap) : c;
-      tile_offsets<D, BS, FP8>(a, nx, o0, o1);
-      load_tile<D, BS, FP8, kNT>(nxt, kp, vp, o0, o1, lane, more);
+      tile_offsets<D, BS, KV>(a, nx, o0, o1);
+      load_tile<D, BS, KV, kNT>(nxt, kp, vp, o0, o1, lane, more);
       st.compute(cur, c.t * kTile, c.L, lg);
       if (!more) return false;
       if (nx.b != c.b || nx.h != c.h) {
@@ -935,15 +946,15 @@ void decode_attn_stream_kernel(AttnArgs a) {
     // are in flight while it is computed.
     Tile t0, t1, t2;
     Cursor n1 = pos + 1 < r1 ? advance(a, c, cap) : c;
-    tile_offsets<D, BS, FP8>(a, c, o0, o1);
-    load_tile<D, BS, FP8, kNT>(t0, kp, vp, o0, o1, lane, true);
-    tile_offsets<D, BS, FP8>(a, n1, o0, o1);
-    load_tile<D, BS, FP8, kNT>(t1, kp, vp, o0, o1, lane, pos + 1 < r1);
+    tile_offsets<D, BS, KV>(a, c, o0, o1);
+    load_tile<D, BS, KV, kNT>(t0, kp, vp, o0, o1, lane, true);
+    tile_offsets<D, BS, KV>(a, n1, o0, o1);
+    load_tile<D, BS, KV, kNT>(t1, kp, vp, o0, o1, lane, pos + 1 < r1);
     auto iter = [&](Tile& cur, Tile& ld) {
       const bool more2 = pos + 2 < r1;
       const Cursor n2 = more2 ? advance(a, n1, cap) : n1;
-      tile_offsets<D, BS, FP8>(a, n2, o0, o1);
-      load_tile<D, BS, FP8, kNT>(ld, kp, vp, o0, o1, lane, more2);
+      tile_offsets<D, BS, KV>(a, n2, o0, o1);
+      load_tile<D, BS, KV, kNT>(ld, kp, vp, o0, o1, lane, more2);
       st.compute(cur, c.t * kTile, c.L, lg);
       if (pos + 1 >= r1) return false;
       if (n1.b != c.b || n1.h != c.h) {
@@ -962,21 +973,22 @@ void decode_attn_stream_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Instances: head_dim {64, 128} x block_size {16, 32, 64} x {fp16, fp8} x
-// group-size class.
-template <int D, int BS, bool FP8, int NH, int NWH, int TW>
+// Instances: head_dim {64, 128} x block_size {16, 32, 64} x {fp16, fp8, int8}
+// x group-size class. Each object file of the library holds one (kind,
+// head_dim) pair (PA_INST_KV, PA_INST_D), so the instances build in parallel.
+template <int D, int BS, int KV, int NH, int NWH, int TW>
 static hipError_t launch_single(const AttnArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((long long)a.B * a.Hkv);
-  hipLaunchKernelGGL((decode_attn_kernel<D, BS, FP8, NH, NWH, TW>), grid,
+  hipLaunchKernelGGL((decode_attn_kernel<D, BS, KV, NH, NWH, TW>), grid,
                      64 * NWH * TW, 0, st, a);
   return hipGetLastError();
 }
 
 // persistent grid: as many workgroups of 4 waves as fit at once on 256 CUs
-template <int D, int BS, bool FP8, int NH, int NWH, bool QL, int SLOTS = 2>
+template <int D, int BS, int KV, int NH, int NWH, bool QL, int SLOTS = 2>
 static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, FP8, NH, NWH, QL, SLOTS>),
-                     256u, NH == 1 && SLOTS == 2 ? 512 : 256, 0, st, a);
+  hipLaunchKernelGGL((decode_attn_stream_kernel<D, BS, KV, NH, NWH, QL, SLOTS>),
+                     (unsigned)kStreamGrid, NH == 1 && SLOTS == 2 ? 512 : 256, 0, st, a);
   return hipGetLastError();
 }
 
@@ -984,44 +996,43 @@ static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
 // of the group's heads (q kept in LDS above 32), two waves (each with its
 // half of the heads) beyond; single pass: head-parallel and token-parallel
 // waves of one workgroup. (Workers: 1024 for fp16 groups of up to 16 heads,
-// 2048 for fp8 ones, 1024 up to 64 heads, 512 beyond.)
-template <int D, int BS, bool FP8>
+// 2048 for one-byte caches, 1024 up to 64 heads, 512 beyond.)
+template <int D, int BS, int KV>
 static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
   if (a.mode >= 2) {
     // up to 16 heads: fp16 tiles run one wave per SIMD with three tiles in
-    // flight; fp8 tiles (half the bytes) two waves per SIMD with two each
+    // flight; one-byte tiles (half the bytes) two waves per SIMD with two
     if (a.G <= 16) {
-      if constexpr (FP8) return launch_stream<D, BS, FP8, 1, 1, false, 2>(a, st);
-      else return launch_stream<D, BS, FP8, 1, 1, false, 3>(a, st);
+      if constexpr (KV != kKvF16) return launch_stream<D, BS, KV, 1, 1, false, 2>(a, st);
+      else return launch_stream<D, BS, KV, 1, 1, false, 3>(a, st);
     }
-    if (a.G <= 32) return launch_stream<D, BS, FP8, 2, 1, false>(a, st);
-    if (a.G <= 64) return launch_stream<D, BS, FP8, 4, 1, true>(a, st);
-    if (a.G <= 96) return launch_stream<D, BS, FP8, 3, 2, false>(a, st);
-    if (a.G <= 128) return launch_stream<D, BS, FP8, 4, 2, true>(a, st);
+    if (a.G <= 32) return launch_stream<D, BS, KV, 2, 1, false>(a, st);
+    if (a.G <= 64) return launch_stream<D, BS, KV, 4, 1, true>(a, st);
+    if (a.G <= 96) return launch_stream<D, BS, KV, 3, 2, false>(a, st);
+    if (a.G <= 128) return launch_stream<D, BS, KV, 4, 2, true>(a, st);
     return hipErrorInvalidValue;
   }
-  if (a.G <= 16) return launch_single<D, BS, FP8, 1, 1, 4>(a, st);
-  if (a.G <= 32) return launch_single<D, BS, FP8, 2, 1, 4>(a, st);
-  if (a.G <= 64) return launch_single<D, BS, FP8, 2, 2, 2>(a, st);
-  if (a.G <= 96) return launch_single<D, BS, FP8, 3, 2, 2>(a, st);
-  if (a.G <= 128) return launch_single<D, BS, FP8, 4, 2, 2>(a, st);
+  if (a.G <= 16) return launch_single<D, BS, KV, 1, 1, 4>(a, st);
+  if (a.G <= 32) return launch_single<D, BS, KV, 2, 1, 4>(a, st);
+  if (a.G <= 64) return launch_single<D, BS, KV, 2, 2, 2>(a, st);
+  if (a.G <= 96) return launch_single<D, BS, KV, 3, 2, 2>(a, st);
+  if (a.G <= 128) return launch_single<D, BS, KV, 4, 2, 2>(a, st);
   return hipErrorInvalidValue;
 }
 
-template <int D, bool FP8>
-static hipError_t launch_bs(const AttnArgs& a, int BS, hipStream_t st) {
+template <int KV, int D>
+hipError_t launch_attn_inst(const AttnArgs& a, int BS, hipStream_t st) {
   switch (BS) {
-    case 16: return launch_group<D, 16, FP8>(a, st);
-    case 32: return launch_group<D, 32, FP8>(a, st);
-    case 64: return launch_group<D, 64, FP8>(a, st);
+    case 16: return launch_group<D, 16, KV>(a, st);
+    case 32: return launch_group<D, 32, KV>(a, st);
+    case 64: return launch_group<D, 64, KV>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attn(const AttnArgs& a, int D, int BS, bool fp8, hipStream_t st) {
-  if (D == 64) return fp8 ? launch_bs<64, true>(a, BS, st) : launch_bs<64, false>(a, BS, st);
-  if (D == 128) return fp8 ? launch_bs<128, true>(a, BS, st) : launch_bs<128, false>(a, BS, st);
-  return hipErrorInvalidValue;
-}
+#if defined(PA_INST_KV) && defined(PA_INST_D)
+template hipError_t launch_attn_inst<PA_INST_KV, PA_INST_D>(const AttnArgs&, int,
+                                                            hipStream_t);
+#endif
 
 }  // namespace pa

@@ -4,9 +4,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launch.h"
+
 namespace pa {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -53,6 +56,52 @@ __device__ __forceinline__ half8 e4m3x8_to_half8(u32x2 w) {
   return as_half8(r);
 }
 
+// Two int8 codes in the low bytes of the two 16-bit halves of `t` become two
+// fp16 values equal to the codes, exactly: with the byte's sign bit flipped
+// (c + 128, 0..255) under the fp16 pattern of 1024 (0x6400) the half reads
+// 1024 + c + 128, and subtracting 1152 leaves c (every integer below 2048 is
+// an fp16 value, so both steps are exact).
+__device__ __forceinline__ uint32_t i8_pair_to_f16_pair(uint32_t t) {
+  const uint32_t biased = (t & 0x00FF00FFu) ^ 0x00800080u;
+  half2v h = __builtin_bit_cast(half2v, biased | 0x64006400u);
+  h = h - half2v{(_Float16)1152.0f, (_Float16)1152.0f};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// Eight int8 codes (two dwords) -> one half8 operand holding the codes.
+__device__ __forceinline__ half8 i8x8_to_half8(u32x2 w) {
+  auto lo = [](uint32_t x) { return i8_pair_to_f16_pair((x & 0xFFu) | ((x & 0xFF00u) << 8)); };
+  auto hi = [](uint32_t x) {
+    return i8_pair_to_f16_pair(((x >> 16) & 0xFFu) | ((x >> 8) & 0xFF0000u));
+  };
+  const u32x4 r = {lo(w.x), hi(w.x), lo(w.y), hi(w.y)};
+  return as_half8(r);
+}
+
+// Eight one-byte codes -> fp16 operand: e4m3fn values times 2^-8, or int8
+// values.
+template <int KV>
+__device__ __forceinline__ half8 codes8_to_half8(u32x2 w) {
+  if constexpr (KV == kKvF8) return e4m3x8_to_half8(w);
+  else return i8x8_to_half8(w);
+}
+
+// Factor that turns the fp16 operand of a code back into code units times
+// the scale: 2^8 for e4m3fn (the bit placement divides by 2^8), 1 for int8.
+template <int KV>
+constexpr float code_unit() {
+  return KV == kKvF8 ? 256.0f : 1.0f;
+}
+
+// float32 -> symmetric int8 code: round to nearest even, saturating at
+// +-127 (the code -128 is never produced), NaN -> 0.
+__device__ __forceinline__ uint32_t f32_to_i8(float y) {
+  if (y != y) return 0u;
+  float r = __builtin_rintf(y);
+  r = r > 127.0f ? 127.0f : (r < -127.0f ? -127.0f : r);
+  return (uint32_t)(int)r & 0xFFu;
+}
+
 // float32 -> OCP e4m3fn code, round to nearest even, saturating: written
 // from the format definition (bias 7, 3 mantissa bits, max 448, min normal
 // 2^-6, subnormal quantum 2^-9, NaN = S.1111.111).
@@ -82,12 +131,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
 // at slot `slot` of the (page, head) tiles ktile / vtile, in the page
 // layout: K rows of each 16-token block in 16-byte chunks with slots 4..7
 // and 8..11 swapped (bits 2 and 3 of the slot exchanged), V as runs of 8
-// tokens per dimension. fp8 tiles receive the e4m3fn codes of
-// value / scale (IEEE fp32 division, round to nearest even, saturating).
-template <int D, bool FP8>
+// tokens per dimension. One-byte tiles receive the codes of value / scale
+// (IEEE fp32 division, then round to nearest even, saturating).
+template <int D, int KV>
 __device__ __forceinline__ void store_kv_pair(uint8_t* ktile, uint8_t* vtile,
                                               int slot, int dp, uint32_t kin,
                                               uint32_t vin, float ks, float vs) {
+  constexpr bool FP8 = KV != kKvF16;                  // one-byte codes
   constexpr int X = FP8 ? 16 : 8;                     // elements per 16 B
   const int blk = slot >> 4, r = slot & 15;
   const int krow = (r & 3) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -102,10 +152,14 @@ __device__ __forceinline__ void store_kv_pair(uint8_t* ktile, uint8_t* vtile,
     auto h2f = [](uint32_t bits) {
       return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
     };
-    const uint32_t k0 = f32_to_e4m3fn(h2f(kin & 0xFFFFu) / ks);
-    const uint32_t k1 = f32_to_e4m3fn(h2f(kin >> 16) / ks);
-    const uint32_t v0 = f32_to_e4m3fn(h2f(vin & 0xFFFFu) / vs);
-    const uint32_t v1 = f32_to_e4m3fn(h2f(vin >> 16) / vs);
+    auto enc = [](float y) {
+      if constexpr (KV == kKvF8) return f32_to_e4m3fn(y);
+      else return f32_to_i8(y);
+    };
+    const uint32_t k0 = enc(h2f(kin & 0xFFFFu) / ks);
+    const uint32_t k1 = enc(h2f(kin >> 16) / ks);
+    const uint32_t v0 = enc(h2f(vin & 0xFFFFu) / vs);
+    const uint32_t v1 = enc(h2f(vin >> 16) / vs);
     *reinterpret_cast<uint16_t*>(ktile + koff) = (uint16_t)(k0 | (k1 << 8));
     vtile[voff] = (uint8_t)v0;
     vtile[voff + 8] = (uint8_t)v1;
@@ -152,6 +206,12 @@ __device__ __forceinline__ float2 load_coherent2(const float* p) {
 // (s_waitcnt vmcnt(0); the other counters are left alone).
 __device__ __forceinline__ void wait_vector_memory() {
   __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Keeps the compiler from moving memory accesses across this point (it emits
+// no instruction): the builtin wait above is not a barrier to the compiler.
+__device__ __forceinline__ void compiler_fence() {
+  asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float read_lane(float v, int src) {

@@ -6,6 +6,15 @@
 
 namespace pa {
 
+// Cache element kinds: fp16 values, or one-byte codes (fp8 e4m3fn, int8)
+// with a per-kv-head fp32 scale for K and one for V.
+enum KvKind : int { kKvF16 = 0, kKvF8 = 1, kKvI8 = 2 };
+
+// The split pass runs a persistent grid of kStreamGrid workgroups with at
+// most 8 waves each, so at most kMaxStreamWorkers workers.
+constexpr int kStreamGrid = 256;
+constexpr int kMaxStreamWorkers = kStreamGrid * 8;
+
 struct KvAppendArgs {
   const uint8_t* k_new;      // fp16 [T, Hkv, D]
   const uint8_t* v_new;
@@ -25,13 +34,14 @@ struct AttnArgs {
   const uint8_t* v_pages;    // [P, Hkv, D, BS] elements
   const int32_t* block_table;
   const int32_t* context_lens;
-  const float* k_scale;      // fp8 only
+  const float* k_scale;      // one-byte caches only
   const float* v_scale;
   _Float16* out;             // single pass: [B, Hq, D]
   float* ws_o;               // split pass: [B, Hq, S, D]
   float* ws_lse;             // split pass: [B, Hq, S]
   int32_t* ws_count;         // split pass: [B, Hkv] partials per (b, h)
-  int32_t* ws_sem;           // merged split pass: [B, Hkv] arrival counters
+  int32_t* ws_sem;           // merged split pass: [kMaxStreamWorkers] arrival
+                             // counters, one per pair, at its first worker
   const _Float16* k_new;     // fused append (else null): [B, Hkv, D] fp16
   const _Float16* v_new;
   const int32_t* positions;  // [B] slot of the new token
@@ -51,10 +61,17 @@ struct ReduceArgs {
   int B, Hq, Hkv, G, S, cap;  // cap = max_blocks * block_size
 };
 
-hipError_t launch_kv_append(const KvAppendArgs& a, int D, bool fp8,
+// kv: KvKind of the cache (device_common.h: 0 fp16, 1 fp8 e4m3fn, 2 int8).
+hipError_t launch_kv_append(const KvAppendArgs& a, int D, int kv,
                             hipStream_t stream);
+hipError_t launch_advance(int32_t* lens, int32_t* positions, int B, int cap,
+                          hipStream_t stream);
+// Attention kernels of one (cache kind, head_dim) pair; each pair is
+// compiled in an object file of its own.
+template <int KV, int D>
+hipError_t launch_attn_inst(const AttnArgs& a, int BS, hipStream_t stream);
 // Returns hipErrorInvalidValue for a shape without a kernel instance.
-hipError_t launch_attn(const AttnArgs& a, int D, int BS, bool fp8,
+hipError_t launch_attn(const AttnArgs& a, int D, int BS, int kv,
                        hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int D, hipStream_t stream);
 

@@ -14,7 +14,7 @@ import pytest
 import paged_mqa_gqa_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "paged_attn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("paged_attn.h", "paged_kv_manager.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(pa.library_path()),
                                 reason="library not built")
@@ -23,9 +23,11 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -34,8 +36,11 @@ def test_header_declares_the_entry_points():
               "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
               "paged_decode_step", "paged_decode_attn_splitk_workspace_size",
               "paged_decode_attn_suggest_splits", "paged_decode_step_fuses_append",
-              "pa_status_string", "pa_version"]:
-        assert n in names
+              "paged_decode_advance",
+              "pa_status_string", "pa_version", "pa_kvm_create", "pa_kvm_plan_step",
+              "pa_kvm_admit", "pa_kvm_release", "pa_kvm_reserve_ahead",
+              "pa_kv_bytes_per_sequence", "pa_kv_pool_bytes"]:
+        assert n in names, n
 
 
 def test_every_declared_symbol_is_exported():
@@ -113,9 +118,38 @@ def test_decode_step_validation():
     assert step(dims=good_dims(num_seqs=1000, kv_dtype=pa.KV_FP8_E4M3FN)) == -3
 
 
-def test_fp8_requires_scales():
-    assert attn(good_dims(kv_dtype=pa.KV_FP8_E4M3FN)) == -3
-    assert attn(good_dims(kv_dtype=pa.KV_FP8_E4M3FN), ks=FAKE) == -3
+@pytest.mark.parametrize("kv", [pa.KV_FP8_E4M3FN, pa.KV_INT8])
+def test_one_byte_caches_require_scales(kv):
+    assert attn(good_dims(kv_dtype=kv)) == -3
+    assert attn(good_dims(kv_dtype=kv), ks=FAKE) == -3
+    assert attn(good_dims(kv_dtype=kv), vs=FAKE) == -3
+    # with both scales the int8 and fp8 kinds pass validation (an empty
+    # batch then returns before any launch)
+    assert attn(good_dims(kv_dtype=kv, num_seqs=0), ks=FAKE, vs=FAKE) == 0
+
+
+def test_workspace_counters_sit_at_a_fixed_offset():
+    """The merged call's arrival counters are the first 2048 int32 of every
+    workspace, whatever the dims and split count: a workspace reused by
+    calls of shrinking or growing size never has partials where another
+    call keeps its counters. The partials follow them."""
+    lib = pa.load()
+    sizes = set()
+    for B, Hq, Hkv, S in ((2, 8, 2, 4), (7, 32, 8, 16), (1, 96, 1, 64), (300, 64, 8, 2)):
+        d = good_dims(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv)
+        n = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), S)
+        rows = B * Hq * S
+        assert n == 2048 * 4 + rows * 128 * 4 + rows * 4 + B * Hkv * 4
+        sizes.add(n)
+        import torch
+        ws = torch.zeros(n, dtype=torch.uint8)
+        o, lse, cnt = pa.split_views(ws, B, Hq, Hkv, S, 128)
+        base = ws.data_ptr()
+        assert o.data_ptr() - base == 2048 * 4
+        assert lse.data_ptr() - base == 2048 * 4 + rows * 128 * 4
+        assert cnt.data_ptr() - base == 2048 * 4 + rows * 128 * 4 + rows * 4
+        assert pa.sem_view(ws).data_ptr() == base and pa.sem_view(ws).numel() == 2048
+    assert len(sizes) == 4
 
 
 def test_empty_batch_is_a_no_op():
@@ -126,7 +160,8 @@ def test_splitk_validation():
     lib = pa.load()
     d = good_dims()
     need = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 4)
-    assert need == 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4 + 2 * 2 * 2 * 4
+    # arrival counters (fixed 2048 slots), o [B,Hq,S,d], lse [B,Hq,S], count [B,Hkv]
+    assert need == 2048 * 4 + 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4 + 2 * 2 * 4
     assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 0) == 0
     call = lambda S, ws, n: lib.paged_decode_attn_splitk(
         ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, S, ws, n, None)

@@ -11,6 +11,7 @@ Contents
   int8       symmetric int8 codes with a per-head scale
   paged      cache append (scatter) and block-table gather
   attention  single-token decode attention, split partials and their merge
+  gemm       the M == 1 decode projection over transposed (fp16 or int8) weights
 
 Sources, by page title and section:
   * "TensorRT对Multi-Query Attention的专项优化支持" (r-odyssey.com/news/246352):
@@ -20,7 +21,9 @@ Sources, by page title and section:
   * "优化" on tiny-llm (open-infra-ai.github.io/tiny-llm/performance/optimization):
     roadmap table, row 分页 KV (block table + scatter/gather, checked token by
     token against contiguous KV) and row FlashDecoding (long-context decode
-    attention, named only); section 3 (GQA: kv heads may differ from q heads).
+    attention, named only); section 3 (GQA: kv heads may differ from q heads);
+    section 4 (the M == 1 GEMM over transposed weights) and section 1 (int8
+    weights with group-wise scales).
   * zyxy.net tag page "tensorrt", FMHA abstract: attention as projections,
     scores, softmax, weighted sum.
 
@@ -29,6 +32,6 @@ against closed forms, library routines (torch SDPA in float64, torch's
 float8_e4m3fn cast, torch's round-half-even and clamp, scipy logsumexp),
 mpmath brute force and invariants.
 """
-from . import fp8, int8, paged, attention  # noqa: F401
+from . import fp8, int8, paged, attention, gemm  # noqa: F401
 from .attention import decode, decode_partials, merge_partials, split_bounds  # noqa: F401
 from .paged import kv_append, gather, empty_pools  # noqa: F401

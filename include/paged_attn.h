@@ -94,11 +94,15 @@ enum pa_status {
   PA_ERR_SPLITS = -4,     /* num_splits outside [1, PA_MAX_SPLITS] */
   PA_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required */
   PA_ERR_HIP = -6,        /* the kernel launch failed */
+  PA_ERR_SCRATCH = -7,    /* the call needs more than the library's static
+                             scratch (PA_STATIC_SCRATCH_BYTES) */
 };
 
 #define PA_MAX_SPLITS 1024
 /* Arrival counters at the start of every split workspace (see below). */
 #define PA_WORKSPACE_SEM_SLOTS 2048
+/* Size of the library's own device scratch (paged_decode_step_static). */
+#define PA_STATIC_SCRATCH_BYTES (32u << 20)
 
 /* Sizes shared by every call on one cache. num_seqs may be 0 (no work). */
 typedef struct pa_dims {
@@ -305,6 +309,32 @@ int paged_decode_step(const pa_dims* dims, const void* q, const void* k_new,
  */
 int paged_decode_advance(const pa_dims* dims, int32_t* context_lens,
                          int32_t* positions, hipStream_t stream);
+
+/*
+ * paged_decode_step_static — paged_decode_step without a caller workspace,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments and result as paged_decode_step minus workspace and
+ * workspace_bytes: the split partials and arrival counters live in a
+ * library-owned device array of PA_STATIC_SCRATCH_BYTES (32 MiB), one per
+ * GPU, held from the library's first use on that GPU until the process
+ * ends. Nothing is allocated by the call. The first call on a GPU looks up
+ * that GPU's copy of the array and enqueues a clear of its arrival counters
+ * on `stream`; every completed call leaves them zero again.
+ * Calls whose paged_decode_attn_splitk_workspace_size(dims, num_splits)
+ * exceeds PA_STATIC_SCRATCH_BYTES return PA_ERR_SCRATCH before anything is
+ * enqueued. All calls on one GPU share the array: two calls that may run at
+ * the same time on one GPU (different streams, or different threads without
+ * ordering) race and give wrong results; order them on one stream.
+ */
+int paged_decode_step_static(const pa_dims* dims, const void* q,
+                             const void* k_new, const void* v_new,
+                             const int32_t* positions, void* k_pages,
+                             void* v_pages, const int32_t* block_table,
+                             const int32_t* context_lens, float scale,
+                             const float* k_scale, const float* v_scale,
+                             int32_t num_splits, void* out, hipStream_t stream);
 
 /* 1 when paged_decode_step with these dims appends inside the attention
  * kernel, 0 when it issues the append as a launch of its own first (more

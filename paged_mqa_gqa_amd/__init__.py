@@ -20,7 +20,7 @@ __all__ = [
     "PaDims", "PagedAttnError", "KV_FP16", "KV_FP8_E4M3FN", "KV_INT8", "library_path",
     "load", "dims", "kv_append", "paged_decode_attn", "paged_decode_attn_splitk",
     "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
-    "paged_decode_step",
+    "paged_decode_step", "paged_decode_step_static", "STATIC_SCRATCH_BYTES",
     "paged_decode_advance",
     "splitk_workspace", "splitk_workspace_size",
     "suggest_splits", "step_fuses_append", "status_string", "version",
@@ -33,6 +33,8 @@ KV_INT8 = 2
 # int32 arrival counters at the start of every split workspace
 # (PA_WORKSPACE_SEM_SLOTS in include/paged_attn.h)
 WORKSPACE_SEM_SLOTS = 2048
+# bytes of the library's own device scratch (PA_STATIC_SCRATCH_BYTES)
+STATIC_SCRATCH_BYTES = 32 << 20
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
 
@@ -76,6 +78,7 @@ def load():
         "paged_decode_attn_splitk_reduce": (I, [D, P, I, P, Z, P, P]),
         "paged_decode_attn_splitk_merged": (I, [D, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
         "paged_decode_step": (I, [D, P, P, P, P, P, P, P, P, F, P, P, I, P, Z, P, P]),
+        "paged_decode_step_static": (I, [D, P, P, P, P, P, P, P, P, F, P, P, I, P, P]),
         "paged_decode_advance": (I, [D, P, P, P]),
         "paged_decode_attn_suggest_splits": (I, [D, I]),
         "paged_decode_step_fuses_append": (I, [D]),
@@ -387,6 +390,27 @@ def paged_decode_advance(context_lens, positions, k_pages, block_table, stream=N
     rc = load().paged_decode_advance(ctypes.byref(d), _ptr(context_lens), _ptr(positions),
                                      _stream(stream))
     _check("paged_decode_advance", rc)
+
+
+def paged_decode_step_static(q, k_new, v_new, positions, k_pages, v_pages, block_table,
+                             context_lens, scale, num_splits, k_scale=None, v_scale=None,
+                             out=None, stream=None):
+    """paged_decode_step without a workspace argument: the library's own
+    static device scratch (STATIC_SCRATCH_BYTES per GPU) holds the split
+    partials, so the call allocates nothing. Calls on one GPU share that
+    scratch and must be ordered on one stream. Returns out."""
+    d, k_scale, v_scale, out = _step_checks(q, k_new, v_new, positions, k_pages, v_pages,
+                                            block_table, context_lens, k_scale, v_scale, out)
+    _on_gpu(q=q, k_new=k_new, v_new=v_new, positions=positions, k_pages=k_pages,
+            v_pages=v_pages, block_table=block_table, context_lens=context_lens,
+            k_scale=k_scale, v_scale=v_scale, out=out)
+    rc = load().paged_decode_step_static(
+        ctypes.byref(d), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(positions),
+        _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(context_lens),
+        float(scale), _ptr(k_scale), _ptr(v_scale), int(num_splits), _ptr(out),
+        _stream(stream))
+    _check("paged_decode_step_static", rc)
+    return out
 
 
 def split_views(workspace, B, Hq, Hkv, S, D):

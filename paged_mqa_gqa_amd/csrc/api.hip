@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace pa {
@@ -262,6 +264,48 @@ int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Library-owned scratch for paged_decode_step_static: the split workspace
+// (arrival counters, partials, counts) of callers that cannot allocate. One
+// copy per GPU (a __device__ array lives in every device's copy of the code
+// object). Host code never uses the array's name as an address: each
+// device's copy is looked up once with hipGetSymbolAddress and that pointer
+// is what the kernels receive.
+static __device__ __align__(256) unsigned char scratch[PA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];        // device address of `scratch`, per GPU
+
+__global__ void zero_words_kernel(int32_t* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// The current GPU's copy of `scratch`. On the first use on a GPU: look it up
+// and enqueue a clear of its arrival counters on `stream` (a kernel, so that
+// the clear is valid inside a graph capture too).
+int scratch_for_current_device(void** out, hipStream_t stream) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return PA_ERR_HIP;
+    hipLaunchKernelGGL(zero_words_kernel, 8, 256, 0, stream, static_cast<int32_t*>(p),
+                       PA_WORKSPACE_SEM_SLOTS);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int kv_append(const pa_dims* dims, int32_t num_tokens, const void* k_new,
@@ -416,6 +460,33 @@ int paged_decode_advance(const pa_dims* dims, int32_t* context_lens, int32_t* po
                                        dims->max_blocks_per_seq * dims->block_size, stream));
 }
 
+int paged_decode_step_static(const pa_dims* dims, const void* q,
+                             const void* k_new, const void* v_new,
+                             const int32_t* positions, void* k_pages,
+                             void* v_pages, const int32_t* block_table,
+                             const int32_t* context_lens, float scale,
+                             const float* k_scale, const float* v_scale,
+                             int32_t num_splits, void* out, hipStream_t stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (num_splits < 1 || num_splits > PA_MAX_SPLITS) return PA_ERR_SPLITS;
+  const size_t need = num_splits > 1 ? ws_bytes(dims, num_splits) : 0;
+  if (need > PA_STATIC_SCRATCH_BYTES) return PA_ERR_SCRATCH;
+  // every other argument is checked before the scratch is touched
+  rc = check_merged(dims, q, k_pages, v_pages, block_table, context_lens, k_scale,
+                    v_scale, num_splits, nullptr, 0, out);
+  if (rc && rc != PA_ERR_WORKSPACE) return rc;
+  if (!k_new || !v_new || !positions) return PA_ERR_NULL;
+  void* ws = nullptr;
+  if (dims->num_seqs > 0 && num_splits > 1) {
+    rc = scratch_for_current_device(&ws, stream);
+    if (rc) return rc;
+  }
+  return paged_decode_step(dims, q, k_new, v_new, positions, k_pages, v_pages,
+                           block_table, context_lens, scale, k_scale, v_scale,
+                           num_splits, ws, PA_STATIC_SCRATCH_BYTES, out, stream);
+}
+
 int32_t paged_decode_step_fuses_append(const pa_dims* dims) {
   const int rc = check_dims(dims);
   if (rc) return rc;
@@ -453,6 +524,7 @@ const char* pa_status_string(int status) {
     case PA_ERR_SPLITS: return "num_splits outside [1, PA_MAX_SPLITS]";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_HIP: return "HIP kernel launch failed";
+    case PA_ERR_SCRATCH: return "the call needs more than the library's static scratch";
     default: return "unknown status";
   }
 }

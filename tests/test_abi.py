@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "paged_decode_attn_splitk_reduce", "paged_decode_attn_splitk_merged",
               "paged_decode_step", "paged_decode_attn_splitk_workspace_size",
               "paged_decode_attn_suggest_splits", "paged_decode_step_fuses_append",
-              "paged_decode_advance",
+              "paged_decode_step_static", "paged_decode_advance",
               "pa_status_string", "pa_version", "pa_kvm_create", "pa_kvm_plan_step",
               "pa_kvm_admit", "pa_kvm_release", "pa_kvm_reserve_ahead",
               "pa_kv_bytes_per_sequence", "pa_kv_pool_bytes"]:
@@ -198,8 +198,33 @@ def test_kv_append_validation():
                          None, FAKE, FAKE, None) == -3
 
 
+def test_static_step_rejects_requests_beyond_its_scratch():
+    """paged_decode_step_static checks every argument and the scratch size
+    before it touches any device: errors come back on a machine with no GPU."""
+    lib = pa.load()
+
+    def call(d, S, out=FAKE, kn=FAKE):
+        return lib.paged_decode_step_static(ctypes.byref(d), FAKE, kn, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, 0.1, None, None, S, out, None)
+    # mixed continuous batch: 256 sequences x 64 q heads x 16 splits of
+    # 129 floats = 135 MB of partials > 32 MiB
+    big = good_dims(num_seqs=256, num_q_heads=64, num_kv_heads=8)
+    assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(big), 16) > 32 << 20
+    assert call(big, 16) == -7
+    assert pa.status_string(-7) != pa.status_string(-99)
+    # a request that fits is checked like paged_decode_step
+    small = good_dims(num_seqs=32, num_q_heads=32, num_kv_heads=8)
+    assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(small), 32) <= 32 << 20
+    assert call(small, 32, out=None) == -1
+    assert call(small, 32, kn=None) == -1
+    assert call(small, 0) == -4
+    assert call(good_dims(head_dim=96), 4) == -2
+    assert call(good_dims(kv_dtype=pa.KV_INT8), 4) == -3
+    assert call(good_dims(num_seqs=0), 4) == 0
+
+
 def test_status_strings_and_version():
-    for s in [0, -1, -2, -3, -4, -5, -6, -99]:
+    for s in [0, -1, -2, -3, -4, -5, -6, -7, -99]:
         assert isinstance(pa.status_string(s), str) and pa.status_string(s)
     assert pa.version() >= 100
 

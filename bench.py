@@ -25,7 +25,12 @@ replays after capture run up to 10% slow (seen on the wide MQA workload);
 the 1000 timed steps then take well under a second on every workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  python bench.py --workload proj_qkv   # a decode projection (M == 1 GEMM)
   python bench.py --copy-only BYTES     # plain copy kernel for counter scaling
+
+A decode-projection workload (proj_qkv, proj_qkv_w8a16, proj_o, lm_head,
+mlp_w8a16_4864) times one gemm_m1_transposed call per step instead, over
+replicas of the transposed weight, against the same HBM roofline.
 """
 from __future__ import annotations
 
@@ -46,6 +51,7 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
                   for f in ("decode_attn.hip", "device_common.h", "launch.h")]
 ATTN_LAUNCHES_PER_GRAPH = 8
+KV_DTYPE_CODE = {"fp16": 0, "fp8_e4m3fn": 1, "int8": 2}     # enum pa_kv_dtype
 
 
 def parse():
@@ -98,8 +104,7 @@ def step_fuses_append(w) -> bool:
     import paged_mqa_gqa_amd as pa
     cfg = w.cfg
     d = pa.PaDims(cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
-                  cfg.block_size, w.num_pages, cfg.max_blocks,
-                  pa.KV_FP16 if cfg.kv_dtype == "fp16" else pa.KV_FP8_E4M3FN)
+                  cfg.block_size, w.num_pages, cfg.max_blocks, KV_DTYPE_CODE[cfg.kv_dtype])
     return pa.step_fuses_append(d)
 
 
@@ -123,14 +128,28 @@ def attention_algorithmic_bytes(w, with_append=True) -> int:
                + cfg.num_seqs * 8 + scales + append)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
 def cpu_baseline(w, budget_s: float):
     """The fp64 oracle, as it stands, on a bounded sample of the same step."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    threads = blas_threads()
     from workloads.device import remap_pages
     cfg = w.cfg
     ks, vs = w.kv_scales()
@@ -160,7 +179,7 @@ def cpu_baseline(w, budget_s: float):
         "sample": f"{seqs_done} of {cfg.num_seqs} sequences of {cfg.name}, one decode "
                   f"step each (append + fp64 attention), {t_total:.1f} s; "
                   f"KV bytes attended / oracle time",
-        "host_cpus": os.cpu_count(),
+        "host_cpus": os.cpu_count(), "cpu_model": cpu_model(),
     }
 
 
@@ -179,23 +198,73 @@ def copy_only(nbytes: int, steps: int):
                       "launches": steps}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported "
-              f"(this library has no multi-GPU path)", file=sys.stderr)
-        sys.exit(2)
-    if args.copy_only:
-        copy_only(args.copy_only, args.steps)
-        return
-    import numpy as np
+def time_graphs(stream, step_graphs, rotation_graph, launch_graph, launches, steps, warmup):
+    """Replay `warmup` then exactly `steps` steps (whole rotations as one graph
+    each, the rest one step graph at a time), synchronised on both sides and
+    timed on the host; then the average duration of one launch from HIP
+    events on `stream` around replays of `launch_graph` (`launches` launches
+    back to back). Returns (ms per step, us per launch)."""
+    import torch
+    R = len(step_graphs)
+
+    def run_steps(k):
+        for _ in range(k // R):
+            rotation_graph.replay()
+        for r in range(k % R):
+            step_graphs[r].replay()
+
+    with torch.cuda.stream(stream):
+        run_steps(warmup)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        run_steps(steps)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    reps = max(4, steps // launches)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        launch_graph.replay()
+        e0.record(stream)
+        for _ in range(reps):
+            launch_graph.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return ms_step, e0.elapsed_time(e1) * 1e3 / (reps * launches)
+
+
+def capture(stream, fn):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
+def split_ranges(pa, dw, S):
+    """Token ranges the split pass actually cuts per (sequence, kv head) for
+    this batch and split cap (read back from one untimed two-pass call)."""
+    import torch
+    if S == 1:
+        return {"max": 1, "mean": 1.0}
+    ws = pa.paged_decode_attn_splitk(dw.q, dw.k_pages, dw.v_pages, dw.block_table,
+                                     dw.context_lens, dw.scale, S, dw.k_scale, dw.v_scale)
+    torch.cuda.synchronize()
+    B, Hq, d = dw.q.shape
+    Hkv = dw.k_pages.shape[1]
+    cnt = pa.split_views(ws, B, Hq, Hkv, S, d)[2].cpu().numpy()
+    live = (dw.context_lens.cpu().numpy() > 0)
+    c = cnt[live]
+    return {"max": int(c.max()), "mean": round(float(c.mean()), 2)}
+
+
+def bench_attention(args):
     import torch
     import paged_mqa_gqa_amd as pa
     from workloads import CONFIGS, Workload
     from workloads.device import DeviceWorkload
 
-    torch.cuda.init()
-    pa.load()
     cfg = CONFIGS[args.workload]
     w = Workload(cfg)
     S = args.splits or cfg.num_splits
@@ -205,6 +274,7 @@ def main():
           f"{R} replica(s), {S} split(s)", file=sys.stderr, flush=True)
 
     dw = DeviceWorkload(w, upto_last=True)
+    ranges = split_ranges(pa, dw, S)
     pools = [(dw.k_pages, dw.v_pages)] + [(dw.k_pages.clone(), dw.v_pages.clone())
                                           for _ in range(R - 1)]
     stream = torch.cuda.Stream()     # the stream every kernel goes to
@@ -235,60 +305,23 @@ def main():
                              dw.block_table, dw.context_lens, dw.scale, S, ws,
                              dw.k_scale, dw.v_scale, out=out, stream=stream)
 
-    def capture(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=stream):
-            fn()
-        return g
-
     # eager run of every call once (first-use work stays out of the graphs)
     with torch.cuda.stream(stream):
         for r in range(R):
             step(r)
     torch.cuda.synchronize()
-    step_graphs = [capture(lambda r=r: step(r)) for r in range(R)]
-    rotation_graph = capture(lambda: [step(r) for r in range(R)])
+    step_graphs = [capture(stream, lambda r=r: step(r)) for r in range(R)]
+    rotation_graph = capture(stream, lambda: [step(r) for r in range(R)])
     # the attention launch on its own: the step itself when the append is
     # fused into it, else the attention call the step makes after its append
     one = step if fused else attention
     with torch.cuda.stream(stream):
         one(0)
     torch.cuda.synchronize()
-    attn_graph = capture(lambda: [one(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
+    attn_graph = capture(stream, lambda: [one(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
     torch.cuda.synchronize()
-
-    def run_steps(k):
-        # k steps: whole rotations as one graph each, the rest one by one
-        for _ in range(k // R):
-            rotation_graph.replay()
-        for r in range(k % R):
-            step_graphs[r].replay()
-
-    with torch.cuda.stream(stream):
-        run_steps(args.warmup)
-    torch.cuda.synchronize()
-
-    # timed region: exactly K steps, synchronised on both sides
-    t0 = time.perf_counter()
-    with torch.cuda.stream(stream):
-        run_steps(args.steps)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-
-    # launch duration of the step's kernel: HIP events on the launch stream
-    # around replays of back-to-back launches (same rotation of pools)
-    reps = max(4, args.steps // ATTN_LAUNCHES_PER_GRAPH)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        attn_graph.replay()
-        e0.record(stream)
-        for _ in range(reps):
-            attn_graph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    attn_avg_us = e0.elapsed_time(e1) * 1e3 / (reps * ATTN_LAUNCHES_PER_GRAPH)
+    ms_step, attn_avg_us = time_graphs(stream, step_graphs, rotation_graph, attn_graph,
+                                       ATTN_LAUNCHES_PER_GRAPH, args.steps, args.warmup)
 
     value = kvb / (ms_step * 1e-3) / 1e9
     alg = attention_algorithmic_bytes(w, with_append=fused)
@@ -308,7 +341,7 @@ def main():
         kernel = "decode_attn_stream_kernel (+ splitk_reduce_kernel)"
     attn_desc += (", kv_append fused into it" if fused
                   else ", kv_append as its own launch before it")
-    res = {
+    return {
         "metric": METRIC,
         "value": round(value, 2),
         "unit": "GB/s",
@@ -319,14 +352,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16" if cfg.kv_dtype == "fp16" else "fp8_e4m3fn",
+        "dtype": cfg.kv_dtype,
         "data": "synthetic (seeded; no dataset or weights involved)",
         "config": {
             "workload": cfg.name, "batch": cfg.num_seqs, "q_heads": cfg.num_q_heads,
             "kv_heads": cfg.num_kv_heads, "head_dim": cfg.head_dim,
             "block_size": cfg.block_size, "kv_dtype": cfg.kv_dtype,
             "context_tokens": int(w.context_lens.sum()), "kv_bytes": int(kvb),
-            "splits": S, "pool_replicas": R,
+            "splits": S, "ranges_per_pair": ranges, "pool_replicas": R,
             "step": f"kv_append + attention ({attn_desc}); the {R} steps of a replica "
                     f"rotation captured as one HIP graph",
         },
@@ -345,6 +378,104 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+
+
+def gemm_cpu_baseline(cfg, x, w, s, budget_s):
+    """The fp64 oracle of the decode projection, as it stands, repeated for
+    about budget_s seconds; weight bytes per second."""
+    from oracle import gemm
+    wt = gemm.transpose(w)
+    st = gemm.transpose(s) if s is not None else None
+    n, t = 0, 0.0
+    while t < budget_s and n < 1000:
+        t0 = time.perf_counter()
+        gemm.gemm_m1(x, wt, st, cfg.group)
+        t += time.perf_counter() - t0
+        n += 1
+    return {"value": round(cfg.weight_bytes * n / t / 1e9, 4), "unit": "GB/s",
+            "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{n} fp64 oracle products of {cfg.name} in {t:.1f} s; weight bytes "
+                      f"/ oracle time (the transposes untimed)",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def bench_gemm(args):
+    import torch
+    import paged_mqa_gqa_amd as pa
+    from workloads import GEMM_CONFIGS, make_gemm
+
+    cfg = GEMM_CONFIGS[args.workload]
+    x, w, s = make_gemm(cfg)
+    R = args.replicas or max(1, min(32, -(-1_000_000_000 // cfg.weight_bytes)))
+    print(f"[bench] {cfg.name}: M {cfg.M} K {cfg.K} N {cfg.N} {cfg.w_dtype}, weights "
+          f"{cfg.weight_bytes / 1e6:.1f} MB, {R} replica(s)", file=sys.stderr, flush=True)
+    xd = torch.from_numpy(x).cuda()
+    wd = torch.from_numpy(w).cuda()
+    sd = torch.from_numpy(s).cuda() if s is not None else None
+    # the load-time transposed copies, R of them so that the 256 MB Infinity
+    # Cache cannot hold the weights a step reads
+    wts = [pa.transpose_weights(wd) for _ in range(R)]
+    sts = [pa.transpose_weights(sd) if sd is not None else None for _ in range(R)]
+    del wd
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.Stream()
+
+    def step(r):
+        pa.gemm_m1_transposed(xd, wts[r], sts[r], cfg.group, out=y, stream=stream)
+
+    with torch.cuda.stream(stream):
+        for r in range(R):
+            step(r)
+    torch.cuda.synchronize()
+    step_graphs = [capture(stream, lambda r=r: step(r)) for r in range(R)]
+    rotation_graph = capture(stream, lambda: [step(r) for r in range(R)])
+    launches = max(8, R)
+    launch_graph = capture(stream, lambda: [step(i % R) for i in range(launches)])
+    torch.cuda.synchronize()
+    ms_step, us_launch = time_graphs(stream, step_graphs, rotation_graph, launch_graph,
+                                     launches, args.steps, args.warmup)
+    alg = cfg.weight_bytes + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2
+    value = alg / (ms_step * 1e-3) / 1e9
+    achieved = alg / (us_launch * 1e-6) / 1e9
+    cpu = None if args.no_cpu_baseline else gemm_cpu_baseline(cfg, x, w, s,
+                                                               min(args.cpu_seconds, 10.0))
+    return {
+        "metric": "decode projection weight GB/s (% of HBM peak) + us/call",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16" if cfg.w_dtype == "fp16" else "int8 weights, fp16 activations",
+        "data": "synthetic (seeded random weights and activations)",
+        "config": {"workload": cfg.name, "M": cfg.M, "K": cfg.K, "N": cfg.N,
+                   "weights": cfg.w_dtype, "group": cfg.group if cfg.w_dtype == "int8" else None,
+                   "weight_bytes": cfg.weight_bytes, "weight_replicas": R,
+                   "step": "one gemm_m1_transposed call; the R calls of a replica rotation "
+                           "captured as one HIP graph"},
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "gemm_m1_kernel",
+                     "algorithmic_bytes_per_launch": alg, "launch_us": round(us_launch, 3)},
+        "cpu_baseline": cpu,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported "
+              f"(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_only:
+        copy_only(args.copy_only, args.steps)
+        return
+    import torch
+    import paged_mqa_gqa_amd as pa
+    from workloads import GEMM_CONFIGS
+    torch.cuda.init()
+    pa.load()
+    res = bench_gemm(args) if args.workload in GEMM_CONFIGS else bench_attention(args)
     print(json.dumps(res), flush=True)
 
 

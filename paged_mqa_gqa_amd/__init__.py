@@ -25,11 +25,14 @@ __all__ = [
     "splitk_workspace", "splitk_workspace_size",
     "suggest_splits", "step_fuses_append", "status_string", "version",
     "KvPageManager", "kv_bytes_per_sequence", "kv_pool_bytes", "kv_pages_for_budget",
+    "W_FP16", "W_INT8", "gemm_m1_transposed", "transpose_weights",
 ]
 
 KV_FP16 = 0
 KV_FP8_E4M3FN = 1
 KV_INT8 = 2
+W_FP16 = 0          # decode projection weights (include/decode_gemm.h)
+W_INT8 = 1
 # int32 arrival counters at the start of every split workspace
 # (PA_WORKSPACE_SEM_SLOTS in include/paged_attn.h)
 WORKSPACE_SEM_SLOTS = 2048
@@ -83,6 +86,9 @@ def load():
         "paged_decode_attn_suggest_splits": (I, [D, I]),
         "paged_decode_step_fuses_append": (I, [D]),
         "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        # decode projection (include/decode_gemm.h)
+        "gemm_m1_transposed": (I, [I, I, I, I, I, P, P, P, P, P]),
+        "transpose_weights": (I, [I, I, I, P, P, P]),
         # page manager (include/paged_kv_manager.h)
         "pa_kv_elem_bytes": (I, [I]),
         "pa_kv_bytes_per_sequence": (ctypes.c_int64, [I, I, I, I, I]),
@@ -410,6 +416,48 @@ def paged_decode_step_static(q, k_new, v_new, positions, k_pages, v_pages, block
         float(scale), _ptr(k_scale), _ptr(v_scale), int(num_splits), _ptr(out),
         _stream(stream))
     _check("paged_decode_step_static", rc)
+    return out
+
+
+def gemm_m1_transposed(x, wt, scales_t=None, group_size=128, out=None, stream=None):
+    """y [M, N] fp16 = x [M, K] fp16 . W for 1 <= M <= 4, with W given
+    transposed as wt [N, K] (fp16, or int8 codes with scales_t [N, K /
+    group_size] fp32). See gemm_m1_transposed in include/decode_gemm.h."""
+    _need(x, "x", torch.float16, 2)
+    M, K = x.shape
+    _need(wt, "wt", (torch.float16, torch.int8), 2)
+    N = wt.shape[0]
+    _need(wt, "wt", shape=(N, K))
+    int8 = wt.dtype == torch.int8
+    if int8:
+        if group_size < 16 or K % group_size:
+            raise ValueError(f"group_size {group_size} must be a multiple of 16 dividing K={K}")
+        _need(scales_t, "scales_t", torch.float32, 2, shape=(N, K // group_size))
+    else:
+        scales_t = None
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _need(out, "out", torch.float16, 2, shape=(M, N))
+    _on_gpu(x=x, wt=wt, scales_t=scales_t, out=out)
+    rc = load().gemm_m1_transposed(M, N, K, W_INT8 if int8 else W_FP16,
+                                   group_size if int8 else 0, _ptr(x), _ptr(wt),
+                                   _ptr(scales_t), _ptr(out), _stream(stream))
+    _check("gemm_m1_transposed", rc)
+    return out
+
+
+def transpose_weights(w, out=None, stream=None):
+    """The [cols, rows] copy of a 2-d tensor w [rows, cols] (elements of 1, 2
+    or 4 bytes), built on the device: the load-time transposed weight (or
+    scales) for gemm_m1_transposed."""
+    _need(w, "w", ndim=2)
+    R, C = w.shape
+    if out is None:
+        out = torch.empty((C, R), dtype=w.dtype, device=w.device)
+    _need(out, "out", w.dtype, 2, shape=(C, R))
+    _on_gpu(w=w, out=out)
+    rc = load().transpose_weights(R, C, w.element_size(), _ptr(w), _ptr(out), _stream(stream))
+    _check("transpose_weights", rc)
     return out
 
 

@@ -21,7 +21,8 @@ LIB_NAME = "libpagedattn.so"
 # once per (cache kind, head_dim) pair, so their instances build in parallel.
 SOURCES = [("api.hip", "api", []), ("kv_append.hip", "kv_append", []),
            ("splitk_reduce.hip", "splitk_reduce", []),
-           ("kv_manager.cpp", "kv_manager", [])] + [
+           ("kv_manager.cpp", "kv_manager", []), ("gemm_m1.hip", "gemm_m1", []),
+           ("gemm_api.hip", "gemm_api", [])] + [
     ("decode_attn.hip", f"decode_attn_{kind}_d{d}", [f"-DPA_INST_KV={kv}", f"-DPA_INST_D={d}"])
     for kv, kind in ((0, "f16"), (1, "f8"), (2, "i8")) for d in (64, 128)]
 ARCH = "gfx950"

@@ -61,6 +61,19 @@ struct ReduceArgs {
   int B, Hq, Hkv, G, S, cap;  // cap = max_blocks * block_size
 };
 
+// Decode projection, M == 1 path (gemm_m1.hip).
+struct GemmArgs {
+  const _Float16* x;         // [M, K]
+  const uint8_t* wt;         // [N, K] fp16 or int8 codes
+  const float* scales_t;     // [N, K / group] (int8 weights only)
+  _Float16* y;               // [M, N]
+  int M, N, K, group;
+};
+
+hipError_t launch_gemm_m1(const GemmArgs& a, bool int8, hipStream_t stream);
+hipError_t launch_transpose(const void* in, void* out, int R, int C, int elem_bytes,
+                            hipStream_t stream);
+
 // kv: KvKind of the cache (device_common.h: 0 fp16, 1 fp8 e4m3fn, 2 int8).
 hipError_t launch_kv_append(const KvAppendArgs& a, int D, int kv,
                             hipStream_t stream);

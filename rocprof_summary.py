@@ -1,7 +1,7 @@
 """Condense rocprofv3 CSV output into the short text summaries kept in profiles/.
 
-  python -m paged_mqa_gqa_amd.rocprof_summary trace DIR --out FILE --command CMD
-  python -m paged_mqa_gqa_amd.rocprof_summary counters --workload NAME \
+  python rocprof_summary.py trace DIR --out FILE --command CMD
+  python rocprof_summary.py counters --workload NAME \
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
       --copy-bytes N --out FILE --command CMD [--kernel decode_attn_stream_kernel]
 
@@ -106,7 +106,7 @@ def _write(path, text):
 
 
 def main(argv=None):
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)

@@ -14,7 +14,8 @@ import pytest
 import paged_mqa_gqa_amd as pa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADERS = [os.path.join(ROOT, "include", h) for h in ("paged_attn.h", "paged_kv_manager.h")]
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in ("paged_attn.h", "paged_kv_manager.h", "decode_gemm.h")]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(pa.library_path()),
                                 reason="library not built")
@@ -39,7 +40,8 @@ def test_header_declares_the_entry_points():
               "paged_decode_step_static", "paged_decode_advance",
               "pa_status_string", "pa_version", "pa_kvm_create", "pa_kvm_plan_step",
               "pa_kvm_admit", "pa_kvm_release", "pa_kvm_reserve_ahead",
-              "pa_kv_bytes_per_sequence", "pa_kv_pool_bytes"]:
+              "pa_kv_bytes_per_sequence", "pa_kv_pool_bytes",
+              "gemm_m1_transposed", "transpose_weights"]:
         assert n in names, n
 
 
@@ -255,3 +257,23 @@ def test_decode_step_fusion_query():
     assert pa.load().paged_decode_step_fuses_append(None) == -1
     with pytest.raises(pa.PagedAttnError):
         pa.step_fuses_append(good_dims(head_dim=96))
+
+
+def test_gemm_validation():
+    """The decode projection's argument checks (no device is touched)."""
+    lib = pa.load()
+    A = ctypes.c_void_p(0x1000)            # 16-byte aligned, never dereferenced
+
+    def call(M=1, N=8, K=64, dt=pa.W_FP16, g=0, x=A, wt=A, sc=None, y=A):
+        return lib.gemm_m1_transposed(M, N, K, dt, g, x, wt, sc, y, None)
+    assert call(M=0) == -2 and call(M=5) == -2 and call(N=0) == -2
+    assert call(K=60) == -2                     # fp16: K % 8
+    assert call(dt=pa.W_INT8, K=72, g=8, sc=A) == -2     # group not a multiple of 16
+    assert call(dt=pa.W_INT8, K=72, g=16, sc=A) == -2    # K not a multiple of the group
+    assert call(dt=pa.W_INT8, K=64, g=16) == -1          # scales missing
+    assert call(dt=7) == -3
+    assert call(M=4, K=8200) == -2                       # activations exceed 64 KB
+    assert call(x=None) == -1 and call(y=None) == -1
+    assert call(x=ctypes.c_void_p(0x1008)) == -2         # x not 16-byte aligned
+    t = lambda R=4, C=4, e=2, w=A, o=A: lib.transpose_weights(R, C, e, w, o, None)
+    assert t(e=3) == -3 and t(R=0) == -2 and t(R=1 << 23) == -2 and t(w=None) == -1

@@ -298,6 +298,58 @@ def arrivals(cfg: Config, count: int, tag: int):
     return lens, prompts
 
 
+@dataclasses.dataclass(frozen=True)
+class GemmConfig:
+    """A decode projection: M activation rows times a [K, N] weight held
+    transposed ([N, K]), fp16 or int8 codes with scales per `group` of k."""
+    name: str
+    M: int
+    K: int
+    N: int
+    w_dtype: str            # "fp16" or "int8"
+    group: int = 128
+    seed: int = 0
+
+    @property
+    def weight_bytes(self) -> int:
+        e = 2 if self.w_dtype == "fp16" else 1
+        s = 0 if self.w_dtype == "fp16" else self.N * (self.K // self.group) * 4
+        return self.N * self.K * e + s
+
+
+GEMM_CONFIGS = {
+    # The projections around the grouped-query attention layer of the
+    # Llama-style workload (32 q / 8 kv heads of 128): QKV (K 4096 -> N
+    # (32 + 2 * 8) * 128 = 6144), fp16 and with int8 weights; the output
+    # projection (4096 -> 4096); a 32000-row vocabulary head.
+    "proj_qkv": GemmConfig("proj_qkv", 1, 4096, 6144, "fp16", seed=2001),
+    "proj_qkv_w8a16": GemmConfig("proj_qkv_w8a16", 1, 4096, 6144, "int8", 128, seed=2002),
+    "proj_o": GemmConfig("proj_o", 1, 4096, 4096, "fp16", seed=2003),
+    "lm_head": GemmConfig("lm_head", 1, 4096, 32000, "fp16", seed=2004),
+    # int8 weights with N = 4864, the width the pages time for their W8A16
+    # M == 1 path (their K is not given; 896 taken, the model width that
+    # goes with a 4864-wide MLP)
+    "mlp_w8a16_4864": GemmConfig("mlp_w8a16_4864", 1, 896, 4864, "int8", 128, seed=2005),
+}
+
+
+def make_gemm(cfg: GemmConfig):
+    """x [M, K] fp16 ~ N(0, 1); the weight as stored before transposition,
+    w [K, N]: fp16 ~ N(0, 1/K) (so y is of order 1), or int8 codes uniform in
+    [-127, 127] with scales [K / group, N] uniform in [0.5, 1.5] / (127
+    sqrt(K / 3)). Returns (x, w, scales or None)."""
+    rng = _stream(cfg.seed, 20)
+    x = rng.standard_normal((cfg.M, cfg.K), dtype=np.float32).astype(np.float16)
+    if cfg.w_dtype == "fp16":
+        w = (rng.standard_normal((cfg.K, cfg.N), dtype=np.float32)
+             / np.float32(math.sqrt(cfg.K))).astype(np.float16)
+        return x, w, None
+    w = rng.integers(-127, 128, (cfg.K, cfg.N), dtype=np.int64).astype(np.int8)
+    s = (rng.uniform(0.5, 1.5, (cfg.K // cfg.group, cfg.N))
+         / (127.0 * math.sqrt(cfg.K / 3.0))).astype(np.float32)
+    return x, w, s
+
+
 def make(name: str, seed: int | None = None, cache_tokens: bool = False) -> Workload:
     return Workload(CONFIGS[name], seed, cache_tokens)
 

@@ -175,16 +175,9 @@ int paged_decode_attn(const pa_dims* dims, const void* q,
  *                                 completed merged call leaves them zero, so
  *                                 one workspace serves calls of any size in
  *                                 turn (each within its own size)
- *   region                        R bytes: the split pass's partials,
- *     o   float32 [B, Hq, S, d]   normalised partial outputs, then
- *     lse float32 [B, Hq, S]      natural-log sum of exp(scores) per partial
- *                                 (the merged call for more than 16 q heads
- *                                 per kv head keeps partials of its own
- *                                 layout here: ceil(G/16) * 16 heads of
- *                                 d + 2 floats per (sequence, kv head, slot))
+ *   o     float32 [B, Hq, S, d]   normalised partial outputs
+ *   lse   float32 [B, Hq, S]      natural-log sum of exp(scores) per partial
  *   count int32   [B, Hkv]        partials written for (sequence, kv head)
- * with R = B*Hq*S*(d+1)*4 for G = Hq/Hkv <= 16, else
- * R = max(B*Hq*S*(d+1), B*Hkv*S*ceil(G/16)*16*(d+2)) * 4.
  * Returns 0 for invalid dims or num_splits.
  */
 size_t paged_decode_attn_splitk_workspace_size(const pa_dims* dims,
@@ -237,18 +230,17 @@ int paged_decode_attn_splitk_reduce(const pa_dims* dims,
 /*
  * paged_decode_attn_splitk_merged — split decode attention in one call.
  *
- * Same kind of split as paged_decode_attn_splitk (ranges of the batch's
- * tiles over a persistent grid, at most num_splits per (sequence, kv head))
- * with the log-sum-exp merge done in the same kernel: a (sequence, kv head)
- * covered by one worker is normalised and written straight to `out`;
- * otherwise each of its workers writes its partial to the workspace with
- * device-scope (write-through) stores, waits for them to complete, and
- * counts its arrival on an arrival counter with a device-scope atomic; the
- * last to arrive reads the partials with device-scope loads, merges them
- * into `out` (in a fixed order, so the bits do not depend on who arrives
- * last) and resets the counter to zero. Groups of more than 16 q heads run
- * a kernel whose workers are 4-wave workgroups sharing each tile through
- * LDS (each wave computes up to 32 of the heads). out [B, Hq, d] fp16
+ * Same split as paged_decode_attn_splitk (ranges of the batch's tiles over
+ * a persistent grid, at most num_splits per (sequence, kv head)), with the
+ * log-sum-exp merge done in the same kernel when the group has at most 16
+ * q heads: a (sequence, kv head) covered by one worker is normalised and
+ * written straight to `out`; otherwise each of its workers writes its
+ * partial to the workspace with device-scope (write-through) stores, waits
+ * for them to complete, and counts its arrival on sem[b, h] with a
+ * device-scope atomic; the last to arrive reads the partials with
+ * device-scope loads, merges them into `out` and resets sem[b, h] to zero.
+ * Larger groups run paged_decode_attn_splitk and then
+ * paged_decode_attn_splitk_reduce on the same stream. out [B, Hq, d] fp16
  * is the same result as paged_decode_attn up to rounding; sequences with
  * L = 0 get zeros. Two merged calls that share one workspace must not run
  * concurrently. num_splits == 1 runs paged_decode_attn (workspace unused).
@@ -265,7 +257,8 @@ int paged_decode_attn_splitk_merged(const pa_dims* dims, const void* q,
 /*
  * paged_decode_step — one decode step: kv_append of every sequence's new
  * token, then paged_decode_attn_splitk_merged over the updated cache, with
- * the append done inside the attention kernel (one launch). Above 1536
+ * the append done inside the attention kernel (one launch for groups of at
+ * most 16 q heads; the reduce kernel follows for wider groups). Above 1536
  * (sequence, kv head) pairs the append is a launch of its own ahead of the
  * attention, where that is faster; every argument is checked before either
  * launch, so a rejected call writes nothing.

@@ -461,28 +461,14 @@ def transpose_weights(w, out=None, stream=None):
     return out
 
 
-def workspace_region_bytes(B, Hq, Hkv, S, D):
-    """Bytes of the partials region that follows the arrival counters: o and
-    lse of the split pass, or for more than 16 q heads per kv head the wide
-    merged call's own partials (ceil(G/16) * 16 heads of D + 2 floats per
-    (sequence, kv head, slot)) if those are larger."""
-    G = Hq // Hkv
-    public = B * Hq * S * (D + 1) * 4
-    if G <= 16:
-        return public
-    wide = B * Hkv * S * (-(-G // 16)) * 16 * (D + 2) * 4
-    return max(public, wide)
-
-
 def split_views(workspace, B, Hq, Hkv, S, D):
     """(o [B,Hq,S,D] f32, lse [B,Hq,S] f32, count [B,Hkv] i32) views of a
     workspace (uint8 tensor), in the header's layout: the arrival counters
-    first (sem_view), then the partials region (o, lse), then count."""
+    first (sem_view), then o, lse and count."""
     n = B * Hq * S
     base = WORKSPACE_SEM_SLOTS * 4
     f = workspace[base:base + (n * D + n) * 4].view(torch.float32)
-    cb = base + workspace_region_bytes(B, Hq, Hkv, S, D)
-    c = workspace[cb:cb + B * Hkv * 4].view(torch.int32)
+    c = workspace[base + (n * D + n) * 4:base + (n * D + n) * 4 + B * Hkv * 4].view(torch.int32)
     return f[:n * D].view(B, Hq, S, D), f[n * D:].view(B, Hq, S), c.view(B, Hkv)
 
 

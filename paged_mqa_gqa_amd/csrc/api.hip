@@ -103,27 +103,16 @@ void apply_fuse(pa::AttnArgs& a, const Fuse* f) {
 
 // Workspace: sem i32 [PA_WORKSPACE_SEM_SLOTS] at a fixed offset (the merged
 // call's arrival counters, left zero by every completed call, so a
-// workspace can serve calls of any size in turn), then the partials region
-// (o f32 [B, Hq, S, D] and lse f32 [B, Hq, S]; the wide-group merged kernel
-// keeps its own partial layout there, which may be larger), then count i32
-// [B, Hkv].
+// workspace can serve calls of any size in turn), then o f32 [B, Hq, S, D],
+// lse f32 [B, Hq, S], count i32 [B, Hkv].
 static_assert(PA_WORKSPACE_SEM_SLOTS >= pa::kMaxStreamWorkers,
               "one arrival counter per split-pass worker");
 constexpr size_t kSemBytes = PA_WORKSPACE_SEM_SLOTS * sizeof(int32_t);
 
-size_t region_bytes(const pa_dims* d, int32_t S) {
-  const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
-  const size_t pub = rows * ((size_t)d->head_dim + 1) * sizeof(float);
-  const int G = d->num_q_heads / d->num_kv_heads;
-  if (G <= 16) return pub;          // only wider groups use the wide layout
-  const size_t wide = (size_t)d->num_seqs * d->num_kv_heads * (size_t)S *
-                      (size_t)pa::wide_partial_floats(G, d->head_dim) * sizeof(float);
-  return pub > wide ? pub : wide;
-}
-
 size_t ws_bytes(const pa_dims* d, int32_t S) {
-  return kSemBytes + region_bytes(d, S) +
-         (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
+  const size_t rows = (size_t)d->num_seqs * d->num_q_heads * (size_t)S;
+  return kSemBytes + rows * (size_t)d->head_dim * sizeof(float) +
+         rows * sizeof(float) + (size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t);
 }
 
 struct WsViews {
@@ -139,7 +128,7 @@ WsViews ws_views(const pa_dims* d, int32_t S, void* ws) {
   v.sem = static_cast<int32_t*>(ws);
   v.o = reinterpret_cast<float*>(static_cast<char*>(ws) + kSemBytes);
   v.lse = v.o + rows * d->head_dim;
-  v.count = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + kSemBytes + region_bytes(d, S));
+  v.count = reinterpret_cast<int32_t*>(v.lse + rows);
   return v;
 }
 
@@ -201,6 +190,10 @@ int split_impl(const pa_dims* dims, const void* q, const void* k_pages,
                                     kv_kind(dims), stream));
 }
 
+// Largest group size (q heads per kv head) whose partials the merged call
+// merges inside the attention kernel.
+constexpr int kMergeInKernelMaxGroup = 16;
+
 // Most (sequence, kv head) pairs for which paged_decode_step appends inside
 // the attention kernel. Each worker owning a new token's tile writes it and
 // waits for the stores before its first tile load; with a pair for nearly
@@ -244,6 +237,16 @@ int merged_impl(const pa_dims* dims, const void* q, const void* k_pages,
   if (num_splits == 1)   // one range per (sequence, kv head): the single pass
     return single_impl(dims, q, k_pages, v_pages, block_table, context_lens,
                        scale, k_scale, v_scale, out, stream, fuse);
+  if (dims->num_q_heads / dims->num_kv_heads > kMergeInKernelMaxGroup) {
+    // wide groups: one wave cannot merge G heads quickly; the reduce kernel
+    // spreads the merge over a wave per (sequence, q head)
+    rc = split_impl(dims, q, k_pages, v_pages, block_table, context_lens, scale,
+                    k_scale, v_scale, num_splits, workspace, workspace_bytes,
+                    stream, fuse);
+    if (rc) return rc;
+    return paged_decode_attn_splitk_reduce(dims, context_lens, num_splits,
+                                           workspace, workspace_bytes, out, stream);
+  }
   pa::AttnArgs a = make_args(dims, q, k_pages, v_pages, block_table,
                              context_lens, scale, k_scale, v_scale);
   const WsViews v = ws_views(dims, num_splits, workspace);

@@ -48,7 +48,6 @@
 #include "device_common.h"
 
 #include <type_traits>
-#include <utility>
 
 namespace pa {
 
@@ -148,7 +147,6 @@ struct HeadState {
   float mrun[NH], lrun[NH];
   f32x4 acc[NH][Gm::kPvMfma];
   float sl, oscale;
-  int live = NH;      // head blocks of this wave inside the group (the rest are skipped)
 
   // q rows of heads (hw*NH + hb)*16 + lane%16 of group h of sequence b as
   // B operands (zeros past the group), softmax state reset.
@@ -229,7 +227,6 @@ struct HeadState {
     }
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
-      if (NH > 1 && hb >= live) break;
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
@@ -636,110 +633,6 @@ __device__ __forceinline__ void tile_offsets(const AttnArgs& a, const Cursor& c,
   }
 }
 
-// The stream-K partition of the batch's tiles over at most `workers`
-// workers: T = total tiles (sequence-major, then kv head, then position;
-// ceil(L/32) tiles per (sequence, kv head)) and W = the workers that get a
-// share. Worker k covers tiles [floor(k T / W), floor((k + 1) T / W)), so
-// every share has floor(T / W) or one more tiles; W is the grid's worker
-// count unless that would cut some (sequence, kv head) into more than S
-// ranges (checked exactly), in which case W is lowered until
-// floor(T / W) >= ceil(n_max / (S - 1)), which bounds every pair by S
-// ranges. W <= T, so every share holds a tile. Every wave computes this
-// redundantly; the results are scalars.
-struct Partition {
-  long long T, W;
-};
-
-__device__ __forceinline__ Partition stream_partition(const AttnArgs& a, int workers,
-                                                      int cap, int lane) {
-  int carry = 0, n_max = 0;
-  for (int c0 = 0; c0 < a.B; c0 += 64) {
-    const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
-    carry += __shfl(wave_incl_sum(n, lane), 63, 64);
-    n_max = max(n_max, wave_max(n));
-  }
-  carry = uniform(carry);
-  n_max = uniform(n_max);
-  const long long T = (long long)carry * a.Hkv;
-  const long long need = (n_max + (a.S - 1) - 1) / (a.S - 1);
-  long long W = workers < T ? workers : T;
-  if (need > 0 && T > 0 && T / need < W) {
-    // the quick bound fails at the full grid: count the ranges exactly
-    int worst = 0;
-    long long done = 0;
-    for (int c0 = 0; c0 < a.B; c0 += 64) {
-      const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
-      const int incl = wave_incl_sum(n, lane);
-      if (n > 0) {
-        const long long x0 = done + (long long)(incl - n) * a.Hkv;
-        for (int h = 0; h < a.Hkv; ++h) {
-          const long long f = ((x0 + (long long)h * n + 1) * W - 1) / T;
-          const long long l = ((x0 + (long long)(h + 1) * n) * W - 1) / T;
-          worst = max(worst, (int)(l - f + 1));
-        }
-      }
-      done += (long long)__shfl(incl, 63, 64) * a.Hkv;
-    }
-    if (uniform(wave_max(worst)) > a.S) W = T / need;
-  }
-  if (W < 1) W = 1;
-  return Partition{T, uniform(W)};
-}
-
-// Sequences without tokens get no share: their zero output (merged call)
-// and their fused append are done here, spread over the workers.
-template <int D, int BS, int KV>
-__device__ __forceinline__ void empty_sequences(const AttnArgs& a, int worker, int workers,
-                                                int cap, int lane) {
-  for (int b = worker; b < a.B; b += workers) {
-    if (clamp_len(a.context_lens[b], cap) != 0) continue;
-    if (a.mode == 3)
-      for (int i = lane; i < a.Hq * D; i += 64)
-        a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
-    if (a.k_new != nullptr) {
-      const int p = load_uniform(a.positions + b);
-      if (p >= 0 && p < cap)
-        for (int h = 0; h < a.Hkv; ++h) append_token<D, BS, KV>(a, b, h, p, lane);
-    }
-  }
-}
-
-// Fused append of a share [r0, r1) whose first and last tiles sit in pairs
-// c and e: the tile of a pair's new token (its last tile if the position
-// lies past the context) that falls in the share is written here, before
-// the share's first tile load; no other worker reads that tile. Only the
-// first and last pairs can extend past the share; pairs between them lie
-// wholly inside it. Returns whether anything was written.
-template <int D, int BS, int KV>
-__device__ __forceinline__ bool append_share(const AttnArgs& a, const Cursor& c,
-                                             const Cursor& e, long long r0, long long r1,
-                                             int cap, int lane) {
-  bool appended = false;                    // scalar: uniform per wave
-  auto append_if_here = [&](const Cursor& s, int p) {
-    if (p < 0 || p >= cap) return;
-    const long long tp = s.base + min(p / kTile, s.n - 1);
-    if (tp >= r0 && tp < r1) {
-      append_token<D, BS, KV>(a, s.b, s.h, p, lane);
-      appended = true;
-    }
-  };
-  const int pc = load_uniform(a.positions + c.b);
-  const int pe = load_uniform(a.positions + e.b);
-  append_if_here(c, pc);
-  if (e.base != c.base) {
-    Cursor s = c;
-    s.t = s.n - 1;
-    s = advance(a, s, cap);                 // first tile of the next pair
-    while (s.base != e.base) {
-      append_if_here(s, load_uniform(a.positions + s.b));
-      s.t = s.n - 1;
-      s = advance(a, s, cap);
-    }
-    append_if_here(e, pe);
-  }
-  return appended;
-}
-
 // Merge the nparts partials of (b, h) from the workspace into out (fp16),
 // one wave: each lane owns 4 output values of one head for up to ITEMS
 // heads at a time and folds the partials in by an online log-sum-exp, in
@@ -828,9 +721,15 @@ __device__ __forceinline__ void merge_partials(const AttnArgs& a, int b, int h,
   }
 }
 
-// Worker k (a wave, or NWH waves with head blocks split between them)
-// streams its share of the stream-K partition (stream_partition). mode 2
-// writes the partials and their count; mode 3 merges too: a
+// Worker k (a wave, or NWH waves with head blocks split between them) of
+// W covers global tiles [floor(k T / W), floor((k + 1) T / W)) of the
+// sequence-major, then kv-head-major, then token order, where each
+// (sequence, kv head) has ceil(L/32) tiles and T is their total. Every
+// share thus has floor(T / W) or one more tiles; W is the grid's worker
+// count unless that would cut some (sequence, kv head) into more than S
+// ranges (checked exactly), in which case W is lowered until
+// floor(T / W) >= ceil(n_max / (S - 1)), which bounds every pair by S
+// ranges. mode 2 writes the partials and their count; mode 3 merges too: a
 // (sequence, kv head) held by one worker is written out directly, otherwise
 // the last of its workers to finish merges the partials (an atomic arrival
 // counter per pair, kept at the index of the pair's first worker and
@@ -858,11 +757,57 @@ void decode_attn_stream_kernel(AttnArgs a) {
   const int worker = blockIdx.x * kWorkersPerWg + wave / NWH;
   const int cap = a.max_blocks * BS;
 
-  // 1. the partition (every wave, redundantly)
-  const Partition pt = stream_partition(a, workers, cap, lane);
-  const long long T = pt.T, W = pt.W;
-  if ((a.mode == 3 || a.k_new != nullptr) && hw == 0)
-    empty_sequences<D, BS, KV>(a, worker, workers, cap, lane);
+  // 1. total tiles and the longest sequence (every wave, redundantly)
+  int carry = 0, n_max = 0;
+  for (int c0 = 0; c0 < a.B; c0 += 64) {
+    const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+    carry += __shfl(wave_incl_sum(n, lane), 63, 64);
+    n_max = max(n_max, wave_max(n));
+  }
+  carry = uniform(carry);
+  n_max = uniform(n_max);
+  const long long T = (long long)carry * a.Hkv;
+  const long long need = (n_max + (a.S - 1) - 1) / (a.S - 1);
+  // never more workers than tiles: every share holds at least one tile, so
+  // the workers between a pair's first and last owner all cover part of it
+  long long W = workers < T ? workers : T;     // (all of these are scalars)
+  if (need > 0 && T > 0 && T / need < W) {
+    // the quick bound fails at the full grid: count the ranges exactly
+    int worst = 0;
+    long long done = 0;
+    for (int c0 = 0; c0 < a.B; c0 += 64) {
+      const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+      const int incl = wave_incl_sum(n, lane);
+      if (n > 0) {
+        const long long x0 = done + (long long)(incl - n) * a.Hkv;
+        for (int h = 0; h < a.Hkv; ++h) {
+          const long long f = ((x0 + (long long)h * n + 1) * W - 1) / T;
+          const long long l = ((x0 + (long long)(h + 1) * n) * W - 1) / T;
+          worst = max(worst, (int)(l - f + 1));
+        }
+      }
+      done += (long long)__shfl(incl, 63, 64) * a.Hkv;
+    }
+    if (uniform(wave_max(worst)) > a.S) W = T / need;
+  }
+  if (W < 1) W = 1;
+  W = uniform(W);
+
+  if ((a.mode == 3 || a.k_new != nullptr) && hw == 0) {
+    // sequences without tokens: no worker covers them, so their zeros and
+    // their fused append are done here
+    for (int b = worker; b < a.B; b += workers) {
+      if (clamp_len(a.context_lens[b], cap) != 0) continue;
+      if (a.mode == 3)
+        for (int i = lane; i < a.Hq * D; i += 64)
+          a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
+      if (a.k_new != nullptr) {
+        const int p = load_uniform(a.positions + b);
+        if (p >= 0 && p < cap)
+          for (int h = 0; h < a.Hkv; ++h) append_token<D, BS, KV>(a, b, h, p, lane);
+      }
+    }
+  }
   if (worker >= W) return;                    // this wave has no share
   const long long r0 = uniform((long long)worker * T / W);
   const long long r1 = uniform((long long)(worker + 1) * T / W);
@@ -883,11 +828,33 @@ void decode_attn_stream_kernel(AttnArgs a) {
   st.begin(a, c.b, c.h, hw, mrow, lg);         // q loads overlap the append
 
   if (a.k_new != nullptr) {
-    // Fused append: the token is written before any tile load and the
-    // worker waits for its own stores, so its loads of that tile see it
-    // (both waves of a two-wave worker write the same bytes). A worker that
-    // wrote nothing goes straight on to its first tile loads.
-    if (append_share<D, BS, KV>(a, c, e, r0, r1, cap, lane)) wait_vector_memory();
+    // Fused append: the worker whose share holds the tile of a pair's new
+    // token (its last tile if the position lies past the context) writes the
+    // token before loading any tile and waits for the stores, so its own
+    // loads of that tile see it. No other worker reads that tile; both
+    // waves of a two-wave worker write the same bytes. The share's first and
+    // last pairs are checked (their positions read together); pairs in
+    // between lie wholly inside the share.
+    auto append_if_here = [&](const Cursor& s, int p) {
+      if (p < 0 || p >= cap) return;
+      const long long tp = s.base + min(p / kTile, s.n - 1);
+      if (tp >= r0 && tp < r1) append_token<D, BS, KV>(a, s.b, s.h, p, lane);
+    };
+    const int pc = load_uniform(a.positions + c.b);
+    const int pe = load_uniform(a.positions + e.b);
+    append_if_here(c, pc);
+    if (e.base != c.base) {
+      Cursor s = c;
+      s.t = s.n - 1;
+      s = advance(a, s, cap);                 // first tile of the next pair
+      while (s.base != e.base) {
+        append_if_here(s, load_uniform(a.positions + s.b));
+        s.t = s.n - 1;
+        s = advance(a, s, cap);
+      }
+      append_if_here(e, pe);
+    }
+    wait_vector_memory();
   }
 
   // End of (b, h)'s segment in this share: partial or output, and merge.
@@ -1006,310 +973,6 @@ void decode_attn_stream_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Wide groups (more than 16 q heads per kv head), merged call.
-//
-// One worker is a workgroup of kWideWaves waves on one CU that stream one
-// share of the stream-K partition together. Wave w computes head blocks
-// 2w, 2w + 1 of the group (waves past the group's blocks only load). Every
-// tile is loaded once: each wave fetches its quarter (16-byte chunks,
-// consecutive lanes on consecutive chunks) into a ring of STAGES register
-// slots, so STAGES tiles are in flight per CU without any wave holding whole
-// tiles, and writes it into one of two LDS tile buffers; after a barrier
-// every wave reads the whole tile from LDS into its matrix-core operands.
-// One barrier per tile: the buffer written at step i was last read at step
-// i - 2, before every wave reached the barrier of step i - 1.
-//
-// A pair split between workers is merged inside the kernel: each wave
-// writes its blocks' raw accumulators in register order (one 1 KB store
-// per 16-dim group) plus each head's running max and sum, counts its
-// arrival on the counter of (pair's first worker, wave index), and the last
-// of the pair's waves with that index folds the partials in slot order (so
-// the result does not depend on which worker arrives last) and writes the
-// output.
-
-constexpr int kWideWaves = 4;
-constexpr int kWideNH = 2;              // head blocks per wave
-#ifndef PA_WIDE_MERGE_BATCH
-#define PA_WIDE_MERGE_BATCH 2
-#endif
-constexpr int kMergeBatch = PA_WIDE_MERGE_BATCH;   // partials loaded together
-
-// f(integral_constant<int, K>{}...) for K in the sequence.
-template <typename F, int... K>
-__device__ __forceinline__ bool expand_steps(F& f, std::integer_sequence<int, K...>) {
-  return f(std::integral_constant<int, K>{}...);
-}
-
-
-template <int D, int BS, int KV, int STAGES>
-__global__ __launch_bounds__(64 * kWideWaves)
-__attribute__((amdgpu_waves_per_eu(1)))
-void decode_attn_wide_kernel(AttnArgs a) {
-  constexpr int NW = kWideWaves, NH = kWideNH;
-  using Gm = Geo<D, BS, KV>;
-  using Tile = TileRegs<D, BS, KV>;
-  using VT = typename Tile::VT;
-  constexpr int kTileBytes = 4 * Gm::kBlockBytes;       // K blocks 0, 1; V blocks 0, 1
-  constexpr int kSegChunks = Gm::kBlockBytes / 16;      // 16-byte chunks per block
-  constexpr int CPL = kTileBytes / 16 / (64 * NW);      // chunks per lane per tile
-  static_assert(CPL >= 1 && kSegChunks % 64 == 0, "tile split over the waves");
-  static_assert(STAGES % 2 == 0, "slot k uses LDS buffer k % 2 on every pass");
-  __shared__ __align__(16) uint8_t tbuf[2][kTileBytes];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = uniform((int)(threadIdx.x >> 6));
-  const int mrow = lane & 15, lg = lane >> 4;
-  const int workers = gridDim.x;
-  const int worker = blockIdx.x;
-  const int cap = a.max_blocks * BS;
-  const int nblocks = (a.G + 15) / 16;
-  const int live = min(max(nblocks - wave * NH, 0), NH);     // scalar
-
-  const Partition pt = stream_partition(a, workers, cap, lane);
-  const long long T = pt.T, W = pt.W;
-  if (wave == 0) empty_sequences<D, BS, KV>(a, worker, workers, cap, lane);
-  if (worker >= W) return;                     // the whole workgroup
-  const long long r0 = uniform((long long)worker * T / W);
-  const long long r1 = uniform((long long)(worker + 1) * T / W);
-  if (r0 >= r1) return;
-  Cursor c = locate(a, r0, cap, lane);
-  const Cursor e = locate(a, r1 - 1, cap, lane);
-  long long fw = worker, lw = worker;
-  if (c.base < r0) fw = uniform(((c.base + 1) * W - 1) / T);
-  if (e.base + e.n > r1) lw = uniform(((e.base + e.n) * W - 1) / T);
-
-  HeadState<D, BS, KV, NH, false> st;
-  st.qsh = nullptr;
-  st.live = live;
-  if (live > 0) st.begin(a, c.b, c.h, wave, mrow, lg);
-  if (a.k_new != nullptr) {
-    // wave 0 writes the share's new tokens and waits for its stores before
-    // any wave of the workgroup loads a tile
-    if (wave == 0 && append_share<D, BS, KV>(a, c, e, r0, r1, cap, lane))
-      wait_vector_memory();
-    workgroup_barrier();
-  }
-
-  // --- finish of a pair's segment: output, or partial + arrival + merge ---
-  // a partial: [block][d/16][64 lanes][4] accumulators, then per block the
-  // 16 heads' running max (log2 units) and sum (wide_partial_floats)
-  const long long part_floats = wide_partial_floats(a.G, D);
-  auto part_ptr = [&](int b, int h, int slot) {
-    return a.ws_o + (((long long)b * a.Hkv + h) * a.S + slot) * part_floats;
-  };
-  // fold the nparts partials of (b, h) (slot order) for this wave's blocks
-  // and write the fp16 output
-  auto merge = [&](int b, int h, int nparts) __attribute__((always_inline)) {
-#pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-      if (hb >= live) break;
-      const int blk = wave * NH + hb;
-      float M = -INFINITY, Ls = 0.0f;           // column head mrow
-      f32x4 racc[Gm::kPvMfma];                  // rows 4 * lg + i
-#pragma unroll
-      for (int jd = 0; jd < Gm::kPvMfma; ++jd) racc[jd] = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
-        f32x4 ap[kMergeBatch][Gm::kPvMfma];
-        float mp[kMergeBatch], lp[kMergeBatch];
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-          const float* base = part_ptr(b, h, min(p0 + u, nparts - 1));
-          const float* o = base + (long long)blk * 16 * D;
-          const float* ml = base + (long long)nblocks * 16 * D + blk * 32;
-#pragma unroll
-          for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-            const float2 x = load_coherent2(o + (jd * 64 + lane) * 4);
-            const float2 y = load_coherent2(o + (jd * 64 + lane) * 4 + 2);
-            ap[u][jd] = f32x4{x.x, x.y, y.x, y.y};
-          }
-          mp[u] = load_coherent(ml + mrow);
-          lp[u] = load_coherent(ml + 16 + mrow);
-        }
-#pragma unroll
-        for (int u = 0; u < kMergeBatch; ++u) {
-          if (p0 + u >= nparts) break;
-          const float Mn = fmaxf(M, mp[u]);
-          const float sa = M == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(M - Mn);
-          const float sp = __builtin_amdgcn_exp2f(mp[u] - Mn);
-          Ls = Ls * sa + lp[u] * sp;
-          M = Mn;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float ra = read_lane(sa, 4 * lg + i), rp = read_lane(sp, 4 * lg + i);
-#pragma unroll
-            for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-              racc[jd][i] = racc[jd][i] * ra + ap[u][jd][i] * rp;
-          }
-        }
-      }
-      // the output scale of the merged pair's own kv head (the head state
-      // may already hold a later pair's)
-      float oscale = 1.0f;
-      if constexpr (Gm::kByte) oscale = load_uniform(a.v_scale + h) * code_unit<KV>();
-      const float inv_col = Ls > 0.0f ? oscale / Ls : 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float inv = read_lane(inv_col, 4 * lg + i);
-        const int hh = blk * 16 + 4 * lg + i;
-        if (hh >= a.G) continue;
-        _Float16* o = a.out + ((long long)b * a.Hq + h * a.G + hh) * D;
-#pragma unroll
-        for (int jd = 0; jd < Gm::kPvMfma; ++jd) o[16 * jd + mrow] = (_Float16)(racc[jd][i] * inv);
-      }
-    }
-  };
-
-  int pend_old = 0;
-  bool pend = false;                            // see the stream kernel: the
-  int pend_b = 0, pend_h = 0, pend_parts = 0;   // share's first pair's arrival
-  long long pend_first = 0;                     // is checked at the share's end
-
-  // at_end false: a pair finished inside the share; it is either this
-  // worker's alone or the share's first pair (held in part, arrival
-  // deferred), so no merge is compiled into the tile loop
-  auto finish = [&](const Cursor& s, auto at_end) __attribute__((always_inline)) {
-    st.reduce_sums();
-    const long long first = s.base < r0 ? fw : worker;
-    const long long last = s.base + s.n > r1 ? lw : worker;
-    if (first == last) {
-      st.write_rows(a, s.b, s.h, wave, -1, mrow, lg);
-      return;
-    }
-    const int slot = (int)(worker - first);
-    const int nparts = (int)(last - first + 1);
-    float* base = part_ptr(s.b, s.h, slot);
-#pragma unroll
-    for (int hb = 0; hb < NH; ++hb) {
-      if (hb >= live) break;
-      const int blk = wave * NH + hb;
-      float* o = base + (long long)blk * 16 * D;
-#pragma unroll
-      for (int jd = 0; jd < Gm::kPvMfma; ++jd) {
-        store_coherent2(o + (jd * 64 + lane) * 4, st.acc[hb][jd][0], st.acc[hb][jd][1]);
-        store_coherent2(o + (jd * 64 + lane) * 4 + 2, st.acc[hb][jd][2], st.acc[hb][jd][3]);
-      }
-      float* ml = base + (long long)nblocks * 16 * D + blk * 32;
-      if (lg == 0) {
-        store_coherent(ml + mrow, st.mrun[hb]);
-        store_coherent(ml + 16 + mrow, st.lrun[hb]);
-      }
-    }
-    compiler_fence();
-    wait_vector_memory();
-    compiler_fence();
-    int* sem = a.ws_sem + first * NW + wave;
-    int old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if constexpr (!decltype(at_end)::value) {
-      pend = true;
-      pend_old = old;
-      pend_b = s.b;
-      pend_h = s.h;
-      pend_parts = nparts;
-      pend_first = first;
-    } else {
-      old = uniform(__shfl(old, 0, 64));
-      if (old == nparts - 1) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        merge(s.b, s.h, nparts);
-        if (lane == 0) __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  };
-
-  // --- the tile pipeline ---
-  const uint8_t* kp = a.k_pages;
-  const uint8_t* vp = a.v_pages;
-  u32x4 stg[STAGES][CPL];
-  Cursor lc = c;              // tile of the next issue
-  long long lpos = r0;        // its index in the share
-  // this wave's chunks of tile lpos into `slot` (past the share's end: one
-  // line per instruction of the last tile, so the wait counts stay exact)
-  auto issue = [&](u32x4 (&slot)[CPL]) __attribute__((always_inline)) {
-    const bool lv = lpos < r1;
-    long long o0, o1;
-    tile_offsets<D, BS, KV>(a, lc, o0, o1);
-#pragma unroll
-    for (int ch = 0; ch < CPL; ++ch) {
-      const int j0 = (ch * NW + wave) * 64;          // first chunk of the instruction
-      const int seg = j0 / kSegChunks;               // 0: K0, 1: K1, 2: V0, 3: V1
-      const int within = j0 % kSegChunks;
-      const uint8_t* blk = (seg < 2 ? kp : vp) + ((seg & 1) ? o1 : o0);
-      slot[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-          blk + (long long)(within + (lv ? lane : 0)) * 16));
-    }
-    if (lv && lpos + 1 < r1) lc = advance(a, lc, cap);
-    ++lpos;
-  };
-  auto stash = [&](const u32x4 (&slot)[CPL], int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ch = 0; ch < CPL; ++ch)
-      *reinterpret_cast<u32x4*>(&tbuf[buf][((ch * NW + wave) * 64 + lane) * 16]) = slot[ch];
-  };
-  // the tile in LDS buffer buf as this wave's operands (load_tile's order,
-  // with the tile's blocks at fixed places)
-  auto read_tile = [&](Tile& t, int buf) __attribute__((always_inline)) {
-    const int R = lane & 15;
-    const uint8_t* kb = &tbuf[buf][0] + (R < 8 ? 0 : Gm::kBlockBytes) + (lg * 16 + (R & 7)) * 16;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int jl = 0; jl < Gm::kKLoads; ++jl)
-        t.k[m][jl] = *reinterpret_cast<const u32x4*>(kb + 128 * m + 1024 * jl);
-    const uint8_t* vb = &tbuf[buf][2 * Gm::kBlockBytes] + (lg < 2 ? 0 : Gm::kBlockBytes) +
-                        ((lg & 1) * 16 + R) * 8 * Gm::kEsz;
-#pragma unroll
-    for (int jd = 0; jd < Gm::kPvMfma; ++jd)
-      t.v[jd] = *reinterpret_cast<const VT*>(vb + jd * 256 * Gm::kEsz);
-  };
-
-  long long pos = r0;
-  auto step = [&](u32x4 (&slot)[CPL], int buf) __attribute__((always_inline)) {
-    stash(slot, buf);             // tile pos (loaded STAGES steps ago) into LDS
-    issue(slot);                  // tile pos + STAGES into the freed slot
-    workgroup_barrier();
-    if (live > 0) {
-      Tile t;
-      read_tile(t, buf);
-      st.compute(t, c.t * kTile, c.L, lg);
-    }
-    if (pos + 1 >= r1) return false;
-    const Cursor nx = advance(a, c, cap);
-    if ((nx.b != c.b || nx.h != c.h) && live > 0) {
-      finish(c, std::false_type{});
-      st.begin(a, nx.b, nx.h, wave, mrow, lg);
-    }
-    ++pos;
-    c = nx;
-    return true;
-  };
-
-#pragma unroll
-  for (int k = 0; k < STAGES; ++k) issue(stg[k]);
-  // one pass = STAGES steps, slot k and LDS buffer k % 2 fixed at compile
-  // time (&& stops at the share's last tile)
-  auto pass = [&](auto... k) __attribute__((always_inline)) {
-    return (step(stg[decltype(k)::value], decltype(k)::value & 1) && ...);
-  };
-  while (expand_steps(pass, std::make_integer_sequence<int, STAGES>{})) {
-  }
-  if (live > 0) {
-    finish(c, std::true_type{});
-    if (pend) {
-      const int old = uniform(__shfl(pend_old, 0, 64));
-      if (old == pend_parts - 1) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        merge(pend_b, pend_h, pend_parts);
-        if (lane == 0)
-          __hip_atomic_store(a.ws_sem + pend_first * NW + wave, 0, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Instances: head_dim {64, 128} x block_size {16, 32, 64} x {fp16, fp8, int8}
 // x group-size class. Each object file of the library holds one (kind,
 // head_dim) pair (PA_INST_KV, PA_INST_D), so the instances build in parallel.
@@ -1329,15 +992,6 @@ static hipError_t launch_stream(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, int BS, int KV>
-static hipError_t launch_wide(const AttnArgs& a, hipStream_t st) {
-  // tiles in flight per CU: six 16 KB fp16 tiles at d = 128, eight otherwise
-  constexpr int kStages = (KV == kKvF16 && D == 128) ? 6 : 8;
-  hipLaunchKernelGGL((decode_attn_wide_kernel<D, BS, KV, kStages>), (unsigned)kStreamGrid,
-                     64 * kWideWaves, 0, st, a);
-  return hipGetLastError();
-}
-
 // Group-size classes. Split pass: one wave streams each tile for up to 64
 // of the group's heads (q kept in LDS above 32), two waves (each with its
 // half of the heads) beyond; single pass: head-parallel and token-parallel
@@ -1345,7 +999,6 @@ static hipError_t launch_wide(const AttnArgs& a, hipStream_t st) {
 // 2048 for one-byte caches, 1024 up to 64 heads, 512 beyond.)
 template <int D, int BS, int KV>
 static hipError_t launch_group(const AttnArgs& a, hipStream_t st) {
-  if (a.mode == 3 && a.G > 16) return launch_wide<D, BS, KV>(a, st);
   if (a.mode >= 2) {
     // up to 16 heads: fp16 tiles run one wave per SIMD with three tiles in
     // flight; one-byte tiles (half the bytes) two waves per SIMD with two

@@ -194,13 +194,6 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
 __device__ __forceinline__ float load_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Two adjacent floats (8-byte aligned) in one device-scope atomic store.
-__device__ __forceinline__ void store_coherent2(float* p, float x, float y) {
-  const unsigned long long v =
-      (unsigned long long)__float_as_uint(x) | ((unsigned long long)__float_as_uint(y) << 32);
-  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), v, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
 // Two adjacent floats (8-byte aligned) in one device-scope atomic load.
 __device__ __forceinline__ float2 load_coherent2(const float* p) {
   const unsigned long long v = __hip_atomic_load(
@@ -219,17 +212,6 @@ __device__ __forceinline__ void wait_vector_memory() {
 // no instruction): the builtin wait above is not a barrier to the compiler.
 __device__ __forceinline__ void compiler_fence() {
   asm volatile("" ::: "memory");
-}
-
-// Barrier of the workgroup's waves after this wave's LDS accesses have
-// completed (s_waitcnt lgkmcnt(0), then s_barrier). Unlike __syncthreads()
-// it does not wait for the wave's global loads, so tiles stay in flight
-// across it; LDS data written before it is visible to every wave after it.
-__device__ __forceinline__ void workgroup_barrier() {
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(0xC07F);     // lgkmcnt(0); vmcnt, expcnt not waited
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
 }
 
 __device__ __forceinline__ float read_lane(float v, int src) {

@@ -15,13 +15,6 @@ enum KvKind : int { kKvF16 = 0, kKvF8 = 1, kKvI8 = 2 };
 constexpr int kStreamGrid = 256;
 constexpr int kMaxStreamWorkers = kStreamGrid * 8;
 
-// Floats of one partial of the wide-group merged kernel (one (sequence, kv
-// head, slot)): raw accumulators of ceil(G/16) blocks of 16 heads in
-// register order, then each head's running max and sum.
-constexpr long long wide_partial_floats(int G, int D) {
-  return (long long)((G + 15) / 16) * 16 * (D + 2);
-}
-
 struct KvAppendArgs {
   const uint8_t* k_new;      // fp16 [T, Hkv, D]
   const uint8_t* v_new;

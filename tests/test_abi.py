@@ -141,10 +141,7 @@ def test_workspace_counters_sit_at_a_fixed_offset():
         d = good_dims(num_seqs=B, num_q_heads=Hq, num_kv_heads=Hkv)
         n = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), S)
         rows = B * Hq * S
-        G = Hq // Hkv
-        region = rows * 129 * 4 if G <= 16 else max(rows * 129 * 4,
-                                                     B * Hkv * S * (-(-G // 16)) * 16 * 130 * 4)
-        assert n == 2048 * 4 + region + B * Hkv * 4
+        assert n == 2048 * 4 + rows * 128 * 4 + rows * 4 + B * Hkv * 4
         sizes.add(n)
         import torch
         ws = torch.zeros(n, dtype=torch.uint8)
@@ -152,7 +149,7 @@ def test_workspace_counters_sit_at_a_fixed_offset():
         base = ws.data_ptr()
         assert o.data_ptr() - base == 2048 * 4
         assert lse.data_ptr() - base == 2048 * 4 + rows * 128 * 4
-        assert cnt.data_ptr() - base == 2048 * 4 + region
+        assert cnt.data_ptr() - base == 2048 * 4 + rows * 128 * 4 + rows * 4
         assert pa.sem_view(ws).data_ptr() == base and pa.sem_view(ws).numel() == 2048
     assert len(sizes) == 4
 
@@ -165,12 +162,8 @@ def test_splitk_validation():
     lib = pa.load()
     d = good_dims()
     need = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 4)
-    # arrival counters (fixed 2048 slots), o [B,Hq,S,d], lse [B,Hq,S] (4 q
-    # heads per kv head: the split pass's layout), count [B,Hkv]
-    assert need == 2048 * 4 + 2 * 8 * 4 * 129 * 4 + 2 * 2 * 4
-    wide = good_dims(num_q_heads=96, num_kv_heads=2)      # 48 heads per kv head
-    need_w = lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(wide), 4)
-    assert need_w == 2048 * 4 + max(2 * 96 * 4 * 129, 2 * 2 * 4 * 48 * 130) * 4 + 2 * 2 * 4
+    # arrival counters (fixed 2048 slots), o [B,Hq,S,d], lse [B,Hq,S], count [B,Hkv]
+    assert need == 2048 * 4 + 2 * 8 * 4 * 128 * 4 + 2 * 8 * 4 * 4 + 2 * 2 * 4
     assert lib.paged_decode_attn_splitk_workspace_size(ctypes.byref(d), 0) == 0
     call = lambda S, ws, n: lib.paged_decode_attn_splitk(
         ctypes.byref(d), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, None, None, S, ws, n, None)

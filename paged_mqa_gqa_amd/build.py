@@ -31,6 +31,9 @@ COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     # keep the compiler from emitting packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # one lane's counter updates stay single atomics: the wave-level
+    # rewrite would wait for each result at once, stalling the tile loads
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

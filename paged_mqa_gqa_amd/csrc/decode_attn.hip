@@ -149,7 +149,9 @@ struct HeadState {
   float sl, oscale;
 
   // q rows of heads (hw*NH + hb)*16 + lane%16 of group h of sequence b as
-  // B operands (zeros past the group), softmax state reset.
+  // B operands, softmax state reset. Rows past the group take the group's
+  // first head (they are computed and never written out), so the loads
+  // need no masking and are not waited for before the first tile's math.
   __device__ __forceinline__ void begin(const AttnArgs& a, int b, int h, int hw,
                                         int mrow, int lg) {
     sl = a.scale_log2;
@@ -161,12 +163,10 @@ struct HeadState {
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
       const int gh = (hw * NH + hb) * 16 + mrow;
-      const bool ok = gh < a.G;
-      const _Float16* qrow = a.q + ((long long)b * a.Hq + h * a.G + (ok ? gh : 0)) * D;
+      const _Float16* qrow = a.q + ((long long)b * a.Hq + h * a.G + (gh < a.G ? gh : 0)) * D;
 #pragma unroll
       for (int jj = 0; jj < Gm::kQkMfma; ++jj) {
-        u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kslot_dim<Gm::kByte>(jj, lg));
-        if (!ok) raw = u32x4{0u, 0u, 0u, 0u};
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + kslot_dim<Gm::kByte>(jj, lg));
         if constexpr (QL) qsh[(hb * Gm::kQkMfma + jj) * 64 + __lane_id()] = raw;
         else qop[hb][jj] = as_half8(raw);
       }

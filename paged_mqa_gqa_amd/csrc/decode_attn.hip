@@ -250,8 +250,7 @@ struct HeadState {
       float mt = sv[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sv[e]);
-      mt = fmaxf(mt, xor_lanes(mt, 16));
-      mt = fmaxf(mt, xor_lanes(mt, 32));
+      mt = max_over_rows(mt);
       // Lazy rescale: the reference max mrun moves only when the tile's max
       // exceeds it by more than kLazyLog2, so probabilities stay <= 2^8
       // (fp16 P and the fp32 sums keep their relative precision) and the
@@ -289,8 +288,7 @@ struct HeadState {
   __device__ __forceinline__ void reduce_sums() {
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
-      lrun[hb] += xor_lanes(lrun[hb], 16);
-      lrun[hb] += xor_lanes(lrun[hb], 32);
+      lrun[hb] = sum_over_rows(lrun[hb]);
     }
   }
 
@@ -540,20 +538,43 @@ __device__ __forceinline__ int seq_tiles(const AttnArgs& a, int b, int cap) {
   return (clamp_len(a.context_lens[b], cap) + kTile - 1) / kTile;
 }
 
-// Inclusive prefix sum across the 64 lanes of a wave.
+// Inclusive prefix sum across the 64 lanes of a wave: a scan inside each
+// 16-lane row by DPP row shifts (a lane with no source lane adds 0), then
+// every row adds the totals of the rows before it, read from their last
+// lanes. VALU and scalar reads only: no LDS round trips.
 __device__ __forceinline__ int wave_incl_sum(int v, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int u = __shfl_up(v, off, 64);
-    if (lane >= off) v += u;
-  }
-  return v;
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(v, 15);
+  const int t1 = __builtin_amdgcn_readlane(v, 31);
+  const int t2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = lane >> 4;
+  return v + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
 }
 
+// Maximum over the 64 lanes (a scalar): a running maximum inside each row
+// (a lane with no source lane keeps its own value), then the rows' last
+// lanes.
 __device__ __forceinline__ int wave_max(int v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  return v;
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false));
+  return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+             max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+}
+
+// Value of lane src (the same for every lane) as a scalar.
+__device__ __forceinline__ int lane_value(int v, int src) {
+  return __builtin_amdgcn_readlane(v, src);
+}
+__device__ __forceinline__ long long lane_value(long long v, int src) {
+  const unsigned long long u = (unsigned long long)v;
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)u, src);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(u >> 32), src);
+  return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
 // Position in the split pass's tile order: (sequence b, kv head h, tile t
@@ -595,13 +616,13 @@ __device__ __forceinline__ Cursor locate(const AttnArgs& a, long long x, int cap
     if (hit) {
       const int src = __ffsll((long long)hit) - 1;
       c.b = c0 + src;
-      c.n = __shfl(n, src, 64);
-      const long long rel = x - __shfl(lo, src, 64);
+      c.n = lane_value(n, src);
+      const long long rel = x - lane_value(lo, src);
       c.h = (int)(rel / c.n);
       c.t = (int)(rel % c.n);
       break;
     }
-    done += (long long)__shfl(incl, 63, 64) * a.Hkv;
+    done += (long long)lane_value(incl, 63) * a.Hkv;
   }
   c.b = uniform(c.b);
   c.h = uniform(c.h);
@@ -761,7 +782,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
   int carry = 0, n_max = 0;
   for (int c0 = 0; c0 < a.B; c0 += 64) {
     const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
-    carry += __shfl(wave_incl_sum(n, lane), 63, 64);
+    carry += lane_value(wave_incl_sum(n, lane), 63);
     n_max = max(n_max, wave_max(n));
   }
   carry = uniform(carry);
@@ -786,7 +807,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
           worst = max(worst, (int)(l - f + 1));
         }
       }
-      done += (long long)__shfl(incl, 63, 64) * a.Hkv;
+      done += (long long)lane_value(incl, 63) * a.Hkv;
     }
     if (uniform(wave_max(worst)) > a.S) W = T / need;
   }

@@ -50,6 +50,8 @@ METRIC = "decode-attn KV GB/s (% of HBM peak) + us/call, GQA 32q/8kv d128 batch 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
                   for f in ("decode_attn.hip", "device_common.h", "launch.h")]
+GEMM_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
+                for f in ("gemm_m1.hip", "device_common.h", "launch.h")]
 ATTN_LAUNCHES_PER_GRAPH = 8
 KV_DTYPE_CODE = {"fp16": 0, "fp8_e4m3fn": 1, "int8": 2}     # enum pa_kv_dtype
 
@@ -71,18 +73,19 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in sources or KERNEL_SOURCES:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILE_DIR, f"decode_attn_{workload}_counters.txt")
+def measured_traffic(workload: str, prefix="decode_attn", sources=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (attention, or with prefix "gemm_m1" and the GEMM sources, the decode
+    projection), if it was taken on the current kernel sources; else None."""
+    path = os.path.join(PROFILE_DIR, f"{prefix}_{workload}_counters.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -90,7 +93,7 @@ def measured_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -399,6 +402,12 @@ def gemm_cpu_baseline(cfg, x, w, s, budget_s):
             "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
+def gemm_algorithmic_bytes(cfg) -> int:
+    """Bytes one decode-projection call must move: the weights (and their
+    group scales), the activation rows in and the fp16 output out."""
+    return cfg.weight_bytes + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2
+
+
 def bench_gemm(args):
     import torch
     import paged_mqa_gqa_amd as pa
@@ -434,8 +443,9 @@ def bench_gemm(args):
     torch.cuda.synchronize()
     ms_step, us_launch = time_graphs(stream, step_graphs, rotation_graph, launch_graph,
                                      launches, args.steps, args.warmup)
-    alg = cfg.weight_bytes + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2
+    alg = gemm_algorithmic_bytes(cfg)
     value = alg / (ms_step * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.name, "gemm_m1", GEMM_SOURCES)
     achieved = alg / (us_launch * 1e-6) / 1e9
     cpu = None if args.no_cpu_baseline else gemm_cpu_baseline(cfg, x, w, s,
                                                                min(args.cpu_seconds, 10.0))
@@ -455,7 +465,7 @@ def bench_gemm(args):
         "us_per_step": round(ms_step * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "gemm_m1_kernel",
+                     "traffic": traffic, "kernel": "gemm_m1_kernel",
                      "algorithmic_bytes_per_launch": alg, "launch_us": round(us_launch, 3)},
         "cpu_baseline": cpu,
     }

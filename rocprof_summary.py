@@ -4,14 +4,18 @@
   python rocprof_summary.py counters --workload NAME \
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
       --copy-bytes N --out FILE --command CMD [--kernel decode_attn_stream_kernel]
+  python rocprof_summary.py pmc DIR --kernel PREFIX --out FILE --command CMD
 
 `trace` keeps the per-kernel statistics of a `--kernel-trace --stats` run.
 `counters` turns FETCH_SIZE / WRITE_SIZE (KiB per dispatch) into HBM bytes
-per launch of the attention kernel: each counter is scaled by the ratio of
+per launch of the attention kernel (or, for a decode-projection workload,
+of gemm_m1_kernel): each counter is scaled by the ratio of
 known bytes to the same counter's reading for a plain copy kernel
 (`bench.py --copy-only N`, which reads N and writes N bytes per launch).
 The summary records the hash of the kernel sources it was taken on;
 bench.py reports the traffic only while that hash still matches.
+`pmc` tabulates the median per dispatch of every counter a `--pmc` run
+collected for the kernels whose name starts with PREFIX.
 """
 from __future__ import annotations
 
@@ -55,8 +59,9 @@ def trace(args):
 
 
 def counters(args):
-    from bench import attention_algorithmic_bytes, kernel_source_hash, step_fuses_append
-    from workloads import CONFIGS, Workload
+    from bench import (GEMM_SOURCES, attention_algorithmic_bytes, gemm_algorithmic_bytes,
+                       kernel_source_hash, step_fuses_append)
+    from workloads import CONFIGS, GEMM_CONFIGS, Workload
     kib = 1024.0
     copy_prefix = "vectorized_elementwise_kernel"
     # the copy run's first elementwise launch converts the source (fp32 ->
@@ -69,15 +74,20 @@ def counters(args):
     aw = _counter_values(args.write, "WRITE_SIZE", args.kernel)
     fetch_b = statistics.median(af) * kib * f_fetch
     write_b = statistics.median(aw) * kib * f_write
-    w = Workload(CONFIGS[args.workload])
-    # the kernel's own bytes: the appended rows only when it does the append
-    alg = attention_algorithmic_bytes(w, with_append=step_fuses_append(w))
+    if args.workload in GEMM_CONFIGS:
+        alg = gemm_algorithmic_bytes(GEMM_CONFIGS[args.workload])
+        src_hash = kernel_source_hash(GEMM_SOURCES)
+    else:
+        w = Workload(CONFIGS[args.workload])
+        # the kernel's own bytes: the appended rows only when it does the append
+        alg = attention_algorithmic_bytes(w, with_append=step_fuses_append(w))
+        src_hash = kernel_source_hash()
     lines = [
         f"# HBM traffic of {args.kernel} on workload {args.workload}",
         f"# command: {args.command}",
         f"kernel: {args.kernel}",
         f"workload: {args.workload}",
-        f"kernel_source_sha256_16: {kernel_source_hash()}",
+        f"kernel_source_sha256_16: {src_hash}",
         f"dispatches_fetch: {len(af)}",
         f"dispatches_write: {len(aw)}",
         f"fetch_size_kib_median: {statistics.median(af):.3f}",
@@ -93,6 +103,22 @@ def counters(args):
         f"algorithmic_bytes_per_launch: {alg}",
         f"traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
     ]
+    _write(args.out, "\n".join(lines) + "\n")
+
+
+def pmc(args):
+    rows = [r for r in csv.DictReader(open(_find(args.dir, "counter_collection.csv")))
+            if r["Kernel_Name"].startswith(args.kernel)]
+    if not rows:
+        raise ValueError(f"no rows for {args.kernel} in {args.dir}")
+    by = {}
+    for r in rows:
+        by.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    lines = [f"# rocprofv3 counters of {args.kernel}* (median per dispatch)",
+             f"# command: {args.command}",
+             f"{'counter':32s} {'dispatches':>10s} {'median':>16s}"]
+    for name in sorted(by):
+        lines.append(f"{name:32s} {len(by[name]):10d} {statistics.median(by[name]):16.1f}")
     _write(args.out, "\n".join(lines) + "\n")
 
 
@@ -122,8 +148,13 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--out", default="-")
     c.add_argument("--command", required=True)
+    m = sub.add_parser("pmc")
+    m.add_argument("dir")
+    m.add_argument("--kernel", required=True)
+    m.add_argument("--out", default="-")
+    m.add_argument("--command", required=True)
     args = ap.parse_args(argv)
-    (trace if args.cmd == "trace" else counters)(args)
+    {"trace": trace, "counters": counters, "pmc": pmc}[args.cmd](args)
 
 
 if __name__ == "__main__":

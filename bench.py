@@ -53,6 +53,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
 GEMM_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
                 for f in ("gemm_m1.hip", "device_common.h", "launch.h")]
 ATTN_LAUNCHES_PER_GRAPH = 8
+LAUNCH_REPS = 5             # repetitions of the per-launch event timing
 KV_DTYPE_CODE = {"fp16": 0, "fp8_e4m3fn": 1, "int8": 2}     # enum pa_kv_dtype
 
 
@@ -206,7 +207,8 @@ def time_graphs(stream, step_graphs, rotation_graph, launch_graph, launches, ste
     each, the rest one step graph at a time), synchronised on both sides and
     timed on the host; then the average duration of one launch from HIP
     events on `stream` around replays of `launch_graph` (`launches` launches
-    back to back). Returns (ms per step, us per launch)."""
+    back to back), measured LAUNCH_REPS times. Returns (ms per step, us per
+    launch as the median of the repetitions, (min, max) of them)."""
     import torch
     R = len(step_graphs)
 
@@ -225,16 +227,20 @@ def time_graphs(stream, step_graphs, rotation_graph, launch_graph, launches, ste
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / steps
     reps = max(4, steps // launches)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        launch_graph.replay()
-        e0.record(stream)
-        for _ in range(reps):
+    samples = []
+    for _ in range(LAUNCH_REPS):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
             launch_graph.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    return ms_step, e0.elapsed_time(e1) * 1e3 / (reps * launches)
+            e0.record(stream)
+            for _ in range(reps):
+                launch_graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3 / (reps * launches))
+    samples.sort()
+    return ms_step, samples[len(samples) // 2], (samples[0], samples[-1])
 
 
 def capture(stream, fn):
@@ -323,7 +329,7 @@ def bench_attention(args):
     torch.cuda.synchronize()
     attn_graph = capture(stream, lambda: [one(i % R) for i in range(ATTN_LAUNCHES_PER_GRAPH)])
     torch.cuda.synchronize()
-    ms_step, attn_avg_us = time_graphs(stream, step_graphs, rotation_graph, attn_graph,
+    ms_step, attn_avg_us, attn_range = time_graphs(stream, step_graphs, rotation_graph, attn_graph,
                                        ATTN_LAUNCHES_PER_GRAPH, args.steps, args.warmup)
 
     value = kvb / (ms_step * 1e-3) / 1e9
@@ -378,6 +384,7 @@ def bench_attention(args):
             "kernel": kernel,
             "algorithmic_bytes_per_launch": alg,
             "launch_us": round(attn_avg_us, 3),
+            "launch_us_min_max": [round(attn_range[0], 3), round(attn_range[1], 3)],
         },
         "cpu_baseline": cpu,
     }
@@ -441,7 +448,7 @@ def bench_gemm(args):
     launches = max(8, R)
     launch_graph = capture(stream, lambda: [step(i % R) for i in range(launches)])
     torch.cuda.synchronize()
-    ms_step, us_launch = time_graphs(stream, step_graphs, rotation_graph, launch_graph,
+    ms_step, us_launch, us_range = time_graphs(stream, step_graphs, rotation_graph, launch_graph,
                                      launches, args.steps, args.warmup)
     alg = gemm_algorithmic_bytes(cfg)
     value = alg / (ms_step * 1e-3) / 1e9
@@ -466,7 +473,8 @@ def bench_gemm(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "gemm_m1_kernel",
-                     "algorithmic_bytes_per_launch": alg, "launch_us": round(us_launch, 3)},
+                     "algorithmic_bytes_per_launch": alg, "launch_us": round(us_launch, 3),
+                     "launch_us_min_max": [round(us_range[0], 3), round(us_range[1], 3)]},
         "cpu_baseline": cpu,
     }
 

@@ -46,10 +46,20 @@ __device__ __forceinline__ void i8x16_to_f16(u32x4 w, u32x4& lo, u32x4& hi) {
   hi = u32x4{pair_lo(w.z), pair_hi(w.z), pair_lo(w.w), pair_hi(w.w)};
 }
 
+// Sum over the 64 lanes (every lane gets it): inside each 16-lane row by
+// DPP (swap neighbours, then pairs, then rotate the row by 4 and by 8),
+// then across the rows with the row swaps. VALU only.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf,
+                                                        false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  v = dpp_add<0xB1>(v);     // quad_perm [1, 0, 3, 2]
+  v = dpp_add<0x4E>(v);     // quad_perm [2, 3, 0, 1]
+  v = dpp_add<0x124>(v);    // row_ror:4
+  v = dpp_add<0x128>(v);    // row_ror:8
+  return sum_over_rows(v);
 }
 
 }  // namespace
@@ -83,6 +93,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_m1_kernel(GemmArgs a) {
     for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
 
   for (int c0 = 0; c0 < wchunks; c0 += 64 * kIter) {
+    // 64-chunk steps of this pass that hold any of the row (the same for
+    // every lane): loads past them are not issued
+    const int steps = min(kIter, (wchunks - c0 + 63) / 64);
     u32x4 w[kRows][kIter];
     float sc[kRows][kIter];
 #pragma unroll
@@ -91,8 +104,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_m1_kernel(GemmArgs a) {
       const u32x4* wr = reinterpret_cast<const u32x4*>(a.wt + row * row_bytes);
 #pragma unroll
       for (int j = 0; j < kIter; ++j) {
-        // chunks past the row's end load its last chunk (in bounds) and are
-        // skipped by the compute loop
+        if (j >= steps) break;
+        // lanes past the row's end inside the last step load its last chunk
+        // (in bounds) and are skipped by the compute loop
         const int ci = min(c0 + j * 64 + lane, wchunks - 1);
         w[r][j] = __builtin_nontemporal_load(wr + ci);
         if constexpr (I8) sc[r][j] = a.scales_t[row * groups + (ci * E) / a.group];
@@ -100,6 +114,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_m1_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < kIter; ++j) {
+      if (j >= steps) break;
       const int ci = c0 + j * 64 + lane;
       if (ci >= wchunks) continue;
       if constexpr (I8) {

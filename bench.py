@@ -48,10 +48,13 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "gqa_llama"
 METRIC = "decode-attn KV GB/s (% of HBM peak) + us/call, GQA 32q/8kv d128 batch 32"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+# what a kernel binary is built from: its sources and the build flags
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
-                  for f in ("decode_attn.hip", "device_common.h", "launch.h")]
+                  for f in ("decode_attn.hip", "device_common.h", "launch.h")] + [
+    os.path.join(ROOT, "paged_mqa_gqa_amd", "build.py")]
 GEMM_SOURCES = [os.path.join(ROOT, "paged_mqa_gqa_amd", "csrc", f)
-                for f in ("gemm_m1.hip", "device_common.h", "launch.h")]
+                for f in ("gemm_m1.hip", "device_common.h", "launch.h")] + [
+    os.path.join(ROOT, "paged_mqa_gqa_amd", "build.py")]
 ATTN_LAUNCHES_PER_GRAPH = 8
 LAUNCH_REPS = 5             # repetitions of the per-launch event timing
 KV_DTYPE_CODE = {"fp16": 0, "fp8_e4m3fn": 1, "int8": 2}     # enum pa_kv_dtype

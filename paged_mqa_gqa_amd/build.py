@@ -17,13 +17,21 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "lib")
 LIB_NAME = "libpagedattn.so"
-# (source, object name, extra defines). The attention kernels are compiled
+# The attention kernels' instruction scheduler: the ILP-first strategy,
+# which re-schedules until the register budget holds. It keeps the wide
+# groups' MFMA, softmax and load streams better interleaved than the
+# default (wide_mqa 74.9 -> 72.4 us per launch, the others unchanged or
+# slightly faster; measured against the default, the max-ILP, the
+# memory-clause and the min-register strategies).
+ATTN_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+# (source, object name, extra flags). The attention kernels are compiled
 # once per (cache kind, head_dim) pair, so their instances build in parallel.
 SOURCES = [("api.hip", "api", []), ("kv_append.hip", "kv_append", []),
            ("splitk_reduce.hip", "splitk_reduce", []),
            ("kv_manager.cpp", "kv_manager", []), ("gemm_m1.hip", "gemm_m1", []),
            ("gemm_api.hip", "gemm_api", [])] + [
-    ("decode_attn.hip", f"decode_attn_{kind}_d{d}", [f"-DPA_INST_KV={kv}", f"-DPA_INST_D={d}"])
+    ("decode_attn.hip", f"decode_attn_{kind}_d{d}",
+     [f"-DPA_INST_KV={kv}", f"-DPA_INST_D={d}", *ATTN_FLAGS])
     for kv, kind in ((0, "f16"), (1, "f8"), (2, "i8")) for d in (64, 128)]
 ARCH = "gfx950"
 

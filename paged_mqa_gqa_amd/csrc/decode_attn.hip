@@ -154,12 +154,14 @@ struct HeadState {
   // need no masking and are not waited for before the first tile's math.
   __device__ __forceinline__ void begin(const AttnArgs& a, int b, int h, int hw,
                                         int mrow, int lg) {
-    sl = a.scale_log2;
-    oscale = 1.0f;
-    if constexpr (Gm::kByte) {
-      sl *= load_uniform(a.k_scale + h) * code_unit<KV>();
-      oscale = load_uniform(a.v_scale + h) * code_unit<KV>();
-    }
+    load_q(a, b, h, hw, mrow, lg);
+    reset(a, h);
+  }
+
+  // The q loads of begin() alone (the previous pair's rows may still be
+  // written out before reset()).
+  __device__ __forceinline__ void load_q(const AttnArgs& a, int b, int h, int hw,
+                                         int mrow, int lg) {
 #pragma unroll
     for (int hb = 0; hb < NH; ++hb) {
       const int gh = (hw * NH + hb) * 16 + mrow;
@@ -170,6 +172,19 @@ struct HeadState {
         if constexpr (QL) qsh[(hb * Gm::kQkMfma + jj) * 64 + __lane_id()] = raw;
         else qop[hb][jj] = as_half8(raw);
       }
+    }
+  }
+
+  // Scales of kv head h and an empty softmax state.
+  __device__ __forceinline__ void reset(const AttnArgs& a, int h) {
+    sl = a.scale_log2;
+    oscale = 1.0f;
+    if constexpr (Gm::kByte) {
+      sl *= load_uniform(a.k_scale + h) * code_unit<KV>();
+      oscale = load_uniform(a.v_scale + h) * code_unit<KV>();
+    }
+#pragma unroll
+    for (int hb = 0; hb < NH; ++hb) {
       mrun[hb] = -INFINITY;
       lrun[hb] = 0.0f;
 #pragma unroll
@@ -878,11 +893,39 @@ void decode_attn_stream_kernel(AttnArgs a) {
     wait_vector_memory();
   }
 
-  // End of (b, h)'s segment in this share: partial or output, and merge.
-  // (AT_END: the share's last pair, merged after the loop two columns per
-  // lane at a time; inside the loop one column keeps register pressure
-  // down. Both fold the partials in the same groups of eight, so the result
-  // does not depend on which worker happens to arrive last.)
+  // Count one arrival (NWH per worker) at the counter of the pair (b, h)
+  // whose first and last owners are `first` and `last`; the last to arrive
+  // merges. Every partial of the pair is stored and waited for (see
+  // finish) before its owner arrives. The counter of a pair is indexed by
+  // its first worker: a worker is the first of at most one pair that
+  // extends past its share (its last pair), so the counters sit at a fixed
+  // place whatever the batch. (AT_END: the share's last pair, merged after
+  // the loop two columns per lane at a time; inside the loop one column
+  // keeps register pressure down. Both fold the partials in the same groups
+  // of eight, so the result does not depend on which worker arrives last.)
+  auto arrive = [&](int b, int h, long long first, long long last, auto at_end) __attribute__((always_inline)) {
+    int old = 0;
+    int* sem = a.ws_sem + first;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = uniform(__shfl(old, 0, 64));
+    const int arrivals = (int)(last - first + 1) * NWH;
+    if (old == arrivals - 1) {
+      // the other workers' partials: visible at the device-coherent level
+      // (their stores completed before their increments); read past this
+      // CU's caches by the device-scope loads of the merge
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if constexpr (decltype(at_end)::value)
+        merge_partials<D, 2>(a, b, h, (int)(last - first + 1), lane);
+      else
+        merge_partials<D, 1>(a, b, h, (int)(last - first + 1), lane);
+      if (lane == 0)
+        __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+
+  // End of (b, h)'s segment in this share: output, or a partial and its
+  // arrival.
   auto finish = [&](const Cursor& s, auto at_end) __attribute__((always_inline)) {
     st.reduce_sums();
     // workers owning the pair's first and last tile
@@ -899,43 +942,39 @@ void decode_attn_stream_kernel(AttnArgs a) {
         a.ws_count[(long long)s.b * a.Hkv + s.h] = slot + 1;
       return;
     }
-    // Publish the partial and count arrivals (NWH per worker); the last to
-    // arrive merges. The partial is written through with device-scope
-    // atomic stores; waiting for their completion before the counter update
-    // makes them visible to whichever compute unit merges, which reads them
-    // with device-scope atomic loads. (A release/acquire pair would instead
+    // The partial is written through with device-scope atomic stores;
+    // waiting for their completion before the counter update makes them
+    // visible to whichever compute unit merges, which reads them with
+    // device-scope atomic loads. (A release/acquire pair would instead
     // write back and invalidate the whole L2 of the XCD at every arrival.)
-    // The counter of a pair is indexed by the pair's first worker: a worker
-    // is the first of at most one pair that extends past its share (its
-    // last pair), so the counters sit at a fixed place whatever the batch.
     st.template write_rows<true>(a, s.b, s.h, hw, slot, mrow, lg);
     compiler_fence();
     wait_vector_memory();
     compiler_fence();
-    int old = 0;
-    int* sem = a.ws_sem + first;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = uniform(__shfl(old, 0, 64));
-    const int arrivals = (int)(last - first + 1) * NWH;
-    if (old == arrivals - 1) {
-      // the other workers' partials: visible at the device-coherent level
-      // (their stores completed before their increments); read past this
-      // CU's caches by the device-scope loads of the merge
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      if constexpr (decltype(at_end)::value)
-        merge_partials<D, 2>(a, s.b, s.h, (int)(last - first + 1), lane);
-      else
-        merge_partials<D, 1>(a, s.b, s.h, (int)(last - first + 1), lane);
-      if (lane == 0)
-        __hip_atomic_store(sem, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    arrive(s.b, s.h, first, last, at_end);
+  };
+
+  // Leave pair s for pair nx inside the loop. Without q in LDS, nx's q loads
+  // go out before s's rows are stored, so the next tile's math waits for
+  // them but not for the stores.
+  auto switch_pair = [&](const Cursor& s, const Cursor& nx) __attribute__((always_inline)) {
+    if constexpr (QL) {
+      finish(s, std::false_type{});
+      st.begin(a, nx.b, nx.h, hw, mrow, lg);
+    } else {
+      st.load_q(a, nx.b, nx.h, hw, mrow, lg);
+      finish(s, std::false_type{});
+      st.reset(a, nx.h);
     }
   };
 
   const uint8_t* kp = a.k_pages;
   const uint8_t* vp = a.v_pages;
   long long o0, o1;
-  long long pos = r0;
+  // The loop counts tiles within the share in 32 bits: 64-bit compares have
+  // no scalar form and would go through vector registers and exec masks.
+  const int ntiles = (int)(r1 - r0);
+  int k = 0;                                  // this share's tile being computed
   constexpr bool kNT = NWH == 1;
   if constexpr (SLOTS == 2) {
     Tile ta, tb;
@@ -946,17 +985,14 @@ void decode_attn_stream_kernel(AttnArgs a) {
     // are issued unconditionally (past the share's end as dead loads) so
     // that the compiler waits only for the older tile.
     auto iter = [&](Tile& cur, Tile& nxt) {
-      const bool more = pos + 1 < r1;
+      const bool more = k + 1 < ntiles;
       const Cursor nx = more ? advance(a, c, cap) : c;
       tile_offsets<D, BS, KV>(a, nx, o0, o1);
       load_tile<D, BS, KV, kNT>(nxt, kp, vp, o0, o1, lane, more);
       st.compute(cur, c.t * kTile, c.L, lg);
       if (!more) return false;
-      if (nx.b != c.b || nx.h != c.h) {
-        finish(c, std::false_type{});
-        st.begin(a, nx.b, nx.h, hw, mrow, lg);
-      }
-      ++pos;
+      if (nx.b != c.b || nx.h != c.h) switch_pair(c, nx);
+      ++k;
       c = nx;
       return true;
     };
@@ -966,23 +1002,20 @@ void decode_attn_stream_kernel(AttnArgs a) {
     // Three register tiles: the loads of the two tiles after the current one
     // are in flight while it is computed.
     Tile t0, t1, t2;
-    Cursor n1 = pos + 1 < r1 ? advance(a, c, cap) : c;
+    Cursor n1 = k + 1 < ntiles ? advance(a, c, cap) : c;
     tile_offsets<D, BS, KV>(a, c, o0, o1);
     load_tile<D, BS, KV, kNT>(t0, kp, vp, o0, o1, lane, true);
     tile_offsets<D, BS, KV>(a, n1, o0, o1);
-    load_tile<D, BS, KV, kNT>(t1, kp, vp, o0, o1, lane, pos + 1 < r1);
+    load_tile<D, BS, KV, kNT>(t1, kp, vp, o0, o1, lane, k + 1 < ntiles);
     auto iter = [&](Tile& cur, Tile& ld) {
-      const bool more2 = pos + 2 < r1;
+      const bool more2 = k + 2 < ntiles;
       const Cursor n2 = more2 ? advance(a, n1, cap) : n1;
       tile_offsets<D, BS, KV>(a, n2, o0, o1);
       load_tile<D, BS, KV, kNT>(ld, kp, vp, o0, o1, lane, more2);
       st.compute(cur, c.t * kTile, c.L, lg);
-      if (pos + 1 >= r1) return false;
-      if (n1.b != c.b || n1.h != c.h) {
-        finish(c, std::false_type{});
-        st.begin(a, n1.b, n1.h, hw, mrow, lg);
-      }
-      ++pos;
+      if (k + 1 >= ntiles) return false;
+      if (n1.b != c.b || n1.h != c.h) switch_pair(c, n1);
+      ++k;
       c = n1;
       n1 = n2;
       return true;

@@ -359,6 +359,15 @@ __device__ __forceinline__ long long uniform(long long v) {
   return (long long)(((unsigned long long)hi << 32) | lo);
 }
 
+// x / y for non-negative x, y > 0, uniform over the wave: a 32-bit
+// division when both fit in 32 bits (gfx9 has no integer divide, and the
+// 64-bit routine is several times longer than the 32-bit one).
+__device__ __forceinline__ long long div_nn(long long x, long long y) {
+  if ((((unsigned long long)x | (unsigned long long)y) >> 32) == 0)
+    return (long long)((unsigned)x / (unsigned)y);
+  return x / y;
+}
+
 __device__ __forceinline__ int clamp_len(int L, int cap) {
   return L < 0 ? 0 : (L > cap ? cap : L);
 }
@@ -618,12 +627,17 @@ __device__ __forceinline__ Cursor advance(const AttnArgs& a, Cursor c, int cap) 
 // The (sequence, kv head) pair holding global tile x of the split order
 // (0 <= x < total tiles): its sequence b, kv head h, tile t within it, its
 // tile count n and the global index of its first tile. Scalar results.
+// len0 holds the clamped lengths of sequences 0..63, one per lane, so a
+// batch of up to 64 sequences is located without a memory round trip.
 __device__ __forceinline__ Cursor locate(const AttnArgs& a, long long x, int cap,
-                                         int lane) {
+                                         int lane, int len0) {
   Cursor c{0, 0, 0, 1, 1, 0};
+  int L = -1;
   long long done = 0;                         // tiles (times Hkv) before chunk
   for (int c0 = 0; c0 < a.B; c0 += 64) {
-    const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+    const int len = c0 == 0 ? len0
+                            : (c0 + lane < a.B ? clamp_len(a.context_lens[c0 + lane], cap) : 0);
+    const int n = (len + kTile - 1) / kTile;
     const int incl = wave_incl_sum(n, lane);
     const long long lo = done + (long long)(incl - n) * a.Hkv;
     const long long hi = done + (long long)incl * a.Hkv;
@@ -632,9 +646,10 @@ __device__ __forceinline__ Cursor locate(const AttnArgs& a, long long x, int cap
       const int src = __ffsll((long long)hit) - 1;
       c.b = c0 + src;
       c.n = lane_value(n, src);
+      L = lane_value(len, src);
       const long long rel = x - lane_value(lo, src);
-      c.h = (int)(rel / c.n);
-      c.t = (int)(rel % c.n);
+      c.h = (int)div_nn(rel, c.n);
+      c.t = (int)(rel - (long long)c.h * c.n);
       break;
     }
     done += (long long)lane_value(incl, 63) * a.Hkv;
@@ -643,7 +658,7 @@ __device__ __forceinline__ Cursor locate(const AttnArgs& a, long long x, int cap
   c.h = uniform(c.h);
   c.t = uniform(c.t);
   c.n = uniform(c.n);
-  c.L = clamp_len(load_uniform(a.context_lens + c.b), cap);
+  c.L = L >= 0 ? uniform(L) : clamp_len(load_uniform(a.context_lens + c.b), cap);
   c.base = x - c.t;
   return c;
 }
@@ -793,10 +808,14 @@ void decode_attn_stream_kernel(AttnArgs a) {
   const int worker = blockIdx.x * kWorkersPerWg + wave / NWH;
   const int cap = a.max_blocks * BS;
 
-  // 1. total tiles and the longest sequence (every wave, redundantly)
+  // 1. total tiles and the longest sequence (every wave, redundantly). The
+  // lengths of the first 64 sequences stay in a register for every later
+  // scan (one load per lane for batches of up to 64 sequences).
+  const int len0 = lane < a.B ? clamp_len(a.context_lens[lane], cap) : 0;
+  const int n0 = (len0 + kTile - 1) / kTile;
   int carry = 0, n_max = 0;
   for (int c0 = 0; c0 < a.B; c0 += 64) {
-    const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+    const int n = c0 == 0 ? n0 : (c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0);
     carry += lane_value(wave_incl_sum(n, lane), 63);
     n_max = max(n_max, wave_max(n));
   }
@@ -812,7 +831,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     int worst = 0;
     long long done = 0;
     for (int c0 = 0; c0 < a.B; c0 += 64) {
-      const int n = c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0;
+      const int n = c0 == 0 ? n0 : (c0 + lane < a.B ? seq_tiles(a, c0 + lane, cap) : 0);
       const int incl = wave_incl_sum(n, lane);
       if (n > 0) {
         const long long x0 = done + (long long)(incl - n) * a.Hkv;
@@ -833,7 +852,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     // sequences without tokens: no worker covers them, so their zeros and
     // their fused append are done here
     for (int b = worker; b < a.B; b += workers) {
-      if (clamp_len(a.context_lens[b], cap) != 0) continue;
+      if ((b < 64 ? lane_value(len0, b) : clamp_len(a.context_lens[b], cap)) != 0) continue;
       if (a.mode == 3)
         for (int i = lane; i < a.Hq * D; i += 64)
           a.out[(long long)b * a.Hq * D + i] = (_Float16)0.0f;
@@ -845,19 +864,19 @@ void decode_attn_stream_kernel(AttnArgs a) {
     }
   }
   if (worker >= W) return;                    // this wave has no share
-  const long long r0 = uniform((long long)worker * T / W);
-  const long long r1 = uniform((long long)(worker + 1) * T / W);
+  const long long r0 = uniform(div_nn((long long)worker * T, W));
+  const long long r1 = uniform(div_nn((long long)(worker + 1) * T, W));
   if (r0 >= r1) return;
 
   // 2. the pairs holding this share's first and last tile. Only those two
   // can extend past the share; the workers owning their far ends (tile x
   // belongs to worker floor(((x + 1) W - 1) / T)) are worked out here, so
   // the loop needs no division.
-  Cursor c = locate(a, r0, cap, lane);
-  const Cursor e = locate(a, r1 - 1, cap, lane);
+  Cursor c = locate(a, r0, cap, lane, len0);
+  const Cursor e = locate(a, r1 - 1, cap, lane, len0);
   long long fw = worker, lw = worker;
-  if (c.base < r0) fw = uniform(((c.base + 1) * W - 1) / T);
-  if (e.base + e.n > r1) lw = uniform(((e.base + e.n) * W - 1) / T);
+  if (c.base < r0) fw = uniform(div_nn((c.base + 1) * W - 1, T));
+  if (e.base + e.n > r1) lw = uniform(div_nn((e.base + e.n) * W - 1, T));
 
   HeadState<D, BS, KV, NH, QL> st;
   st.qsh = qsmem[wave];
@@ -908,7 +927,7 @@ void decode_attn_stream_kernel(AttnArgs a) {
     int* sem = a.ws_sem + first;
     if (lane == 0)
       old = __hip_atomic_fetch_add(sem, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = uniform(__shfl(old, 0, 64));
+    old = __builtin_amdgcn_readlane(old, 0);   // lane 0 holds the result
     const int arrivals = (int)(last - first + 1) * NWH;
     if (old == arrivals - 1) {
       // the other workers' partials: visible at the device-coherent level
@@ -976,6 +995,12 @@ void decode_attn_stream_kernel(AttnArgs a) {
   const int ntiles = (int)(r1 - r0);
   int k = 0;                                  // this share's tile being computed
   constexpr bool kNT = NWH == 1;
+  // The loop runs whole passes of SLOTS steps and leaves only at the bottom
+  // of a pass. A step past the share's last tile issues its dead load and
+  // computes nothing, so every step of a pass sees the same loads in flight
+  // and the compiler's waits stay exact (an exit after each step would merge
+  // the register state of every exit into the loop's flow and drain the
+  // loads once per pass).
   if constexpr (SLOTS == 2) {
     Tile ta, tb;
     tile_offsets<D, BS, KV>(a, c, o0, o1);
@@ -984,20 +1009,22 @@ void decode_attn_stream_kernel(AttnArgs a) {
     // next segment) are in flight while the current tile is computed. They
     // are issued unconditionally (past the share's end as dead loads) so
     // that the compiler waits only for the older tile.
-    auto iter = [&](Tile& cur, Tile& nxt) {
+    auto step = [&](Tile& cur, Tile& nxt) __attribute__((always_inline)) {
       const bool more = k + 1 < ntiles;
       const Cursor nx = more ? advance(a, c, cap) : c;
       tile_offsets<D, BS, KV>(a, nx, o0, o1);
       load_tile<D, BS, KV, kNT>(nxt, kp, vp, o0, o1, lane, more);
-      st.compute(cur, c.t * kTile, c.L, lg);
-      if (!more) return false;
-      if (nx.b != c.b || nx.h != c.h) switch_pair(c, nx);
+      if (k < ntiles) {
+        st.compute(cur, c.t * kTile, c.L, lg);
+        if (more && (nx.b != c.b || nx.h != c.h)) switch_pair(c, nx);
+      }
       ++k;
       c = nx;
-      return true;
     };
-    while (iter(ta, tb) && iter(tb, ta)) {
-    }
+    do {
+      step(ta, tb);
+      step(tb, ta);
+    } while (k < ntiles);
   } else {
     // Three register tiles: the loads of the two tiles after the current one
     // are in flight while it is computed.
@@ -1007,21 +1034,24 @@ void decode_attn_stream_kernel(AttnArgs a) {
     load_tile<D, BS, KV, kNT>(t0, kp, vp, o0, o1, lane, true);
     tile_offsets<D, BS, KV>(a, n1, o0, o1);
     load_tile<D, BS, KV, kNT>(t1, kp, vp, o0, o1, lane, k + 1 < ntiles);
-    auto iter = [&](Tile& cur, Tile& ld) {
+    auto step = [&](Tile& cur, Tile& ld) __attribute__((always_inline)) {
       const bool more2 = k + 2 < ntiles;
       const Cursor n2 = more2 ? advance(a, n1, cap) : n1;
       tile_offsets<D, BS, KV>(a, n2, o0, o1);
       load_tile<D, BS, KV, kNT>(ld, kp, vp, o0, o1, lane, more2);
-      st.compute(cur, c.t * kTile, c.L, lg);
-      if (k + 1 >= ntiles) return false;
-      if (n1.b != c.b || n1.h != c.h) switch_pair(c, n1);
+      if (k < ntiles) {
+        st.compute(cur, c.t * kTile, c.L, lg);
+        if (k + 1 < ntiles && (n1.b != c.b || n1.h != c.h)) switch_pair(c, n1);
+      }
       ++k;
       c = n1;
       n1 = n2;
-      return true;
     };
-    while (iter(t0, t2) && iter(t1, t0) && iter(t2, t1)) {
-    }
+    do {
+      step(t0, t2);
+      step(t1, t0);
+      step(t2, t1);
+    } while (k < ntiles);
   }
   finish(c, std::true_type{});
 }

@@ -23,7 +23,15 @@ LIB_NAME = "libpagedattn.so"
 # default (wide_mqa 74.9 -> 72.4 us per launch, the others unchanged or
 # slightly faster; measured against the default, the max-ILP, the
 # memory-clause and the min-register strategies).
-ATTN_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]
+# MFMA accumulators in VGPRs (the "VGPR form" of the matrix instructions):
+# with the default choice the compiler keeps the P.V accumulators in AGPRs,
+# lends those AGPRs to the QK^T results and copies every accumulator out to
+# VGPRs and back once per tile. In VGPR form the copies are gone and the
+# register total drops (96-head worker 436 -> 352, 16-head worker
+# 328 -> 297): wide_mqa 74.6 -> 66.3 us per launch, gqa_llama 50.9 -> 50.5,
+# mixed_fp8 unchanged (A/B on one box, two repetitions each).
+ATTN_FLAGS = ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
+              "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 # (source, object name, extra flags). The attention kernels are compiled
 # once per (cache kind, head_dim) pair, so their instances build in parallel.
 SOURCES = [("api.hip", "api", []), ("kv_append.hip", "kv_append", []),
